@@ -1,0 +1,397 @@
+"""CPU oracle for the SageAttention-style 8-bit attention forward.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call this module.  The
+product path (``quantized_attention_quant_amd``) never imports it and shares
+no code with it: the two agree only because both follow the same pages.
+
+The oracle is deliberately plain: numpy, no blocking or fusion beyond what the
+method itself defines, fp64 for the attention arithmetic.  Where floating point
+decides an integer (the INT8 and e4m3 codes of Q, K and V) the decision is
+taken in fp32, the precision the GPU path uses, so those codes are comparable
+bit for bit.
+
+Pages cited (by title; sections as they appear on each page)
+  [PS]  "⚡️SageAttention — brand new attention" (postsniper.ru): the
+        quantisation introduction (scale = max|A|/127, round(A/scale),
+        C ≈ (ÂB̂)(δAδB)), the outlier example, the SageAttention bullets
+        (INT8 QKᵀ with K normalisation, fused scaling, FP16 PV) and the
+        SageAttention2 bullets (FP8 PV stabilised with FP32 double buffering).
+  [DT]  dtcms.com SageAttention summary: section "SageAttention（v1）"
+        (smooth K by subtracting its mean; per-block or per-token Q/K
+        quantisation) and section "SageAttention 2" (P and V in FP8, two-level
+        accumulation for FP8 PV).
+  [IP]  "Attention机制优化：从FlashAttention到SageAttention的工程实践"
+        (intelliparadigm.com): §2.1 (Attn = softmax(QKᵀ/√d)V) and §3.1
+        (tiling, kernel fusion, online softmax).
+  [CS]  deepseek.csdn.net post on using sageattn in DeepSeek-VL2: the attention
+        forward that transposes to [B, H, N, d] and calls sageattn with
+        is_causal=True.
+
+Readings where the pages are silent (each listed in the design notes):
+  * block geometry: Q blocks of 128 tokens, K blocks of 64 tokens, all d
+    channels, never crossing a sequence; the last block is partial;
+  * K mean: exact int64 fixed-point column sum (every fp16 is a multiple of
+    2^-24), one fp64 divide by n, one rounding to fp32; domain = one
+    (sequence, head);
+  * smoothed K stays in fp32 (not re-rounded to fp16);
+  * round = round-half-to-even; clamp to ±127; an all-zero block has scale 0
+    and codes 0;
+  * the softmax scale (fp32 of 1/sqrt(d) computed in fp64) is multiplied into
+    Q's emitted block scale after quantisation;
+  * online softmax walks 64-key tiles in ascending order, updating the row max
+    once per tile (the FP8 P codes depend on this schedule);
+  * FP8 mode: V per-channel scale amax/448, codes OCP e4m3 (bias 7, max 448,
+    round to nearest even, saturate to ±448); P codes are e4m3(p * 448);
+    level 1 sums one tile's P̂V̂, level 2 is the running output;
+  * the row sum l is taken from the unrounded p.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+Q_BLOCK = 128      # tokens per Q quantisation block
+K_BLOCK = 64       # tokens per K quantisation block
+KV_TILE = 64       # keys per online-softmax step
+INT8_MAX = 127
+E4M3_MAX = 448.0
+FIXED_POINT_SHIFT = 24   # fp16 values are integer multiples of 2^-24
+
+__all__ = [
+    "Q_BLOCK", "K_BLOCK", "KV_TILE", "default_sm_scale", "k_token_mean", "smooth_k",
+    "quantize_int8_blocks", "quant_q", "quant_k", "quant_qk_dense", "quant_qk_varlen",
+    "e4m3_decode", "e4m3_encode", "quant_v_fp8", "quant_v_fp8_dense", "quant_v_fp8_varlen",
+    "qk_int", "sage_attention_rows", "sdpa_fp64_rows", "head_views_dense",
+    "head_views_varlen",
+]
+
+
+# ----------------------------------------------------------------------------
+# Scale of the softmax
+# ----------------------------------------------------------------------------
+def default_sm_scale(d: int) -> np.float32:
+    """Softmax scale 1/sqrt(d) of [IP] §2.1, computed in fp64 and rounded once to fp32."""
+    return np.float32(1.0 / math.sqrt(d))
+
+
+# ----------------------------------------------------------------------------
+# K smoothing ([DT] "SageAttention（v1）" first bullet; [PS] SageAttention bullets)
+# ----------------------------------------------------------------------------
+def k_token_mean(k: np.ndarray) -> np.ndarray:
+    """Mean of K over its tokens, per channel: k fp16 [..., n, d] -> fp32 [..., d].
+
+    [DT] "SageAttention（v1）": K is smoothed by subtracting its mean.  The sum
+    is exact: each fp16 value times 2^24 is an integer, summed in int64, then
+    divided by n once in fp64 and rounded once to fp32.
+    """
+    if k.dtype != np.float16:
+        raise TypeError("k must be fp16")
+    n = k.shape[-2]
+    if n == 0:
+        raise ValueError("empty sequence")
+    fixed = (k.astype(np.float64) * float(2 ** FIXED_POINT_SHIFT)).astype(np.int64)
+    total = fixed.sum(axis=-2, dtype=np.int64)
+    mean64 = total.astype(np.float64) * (2.0 ** -FIXED_POINT_SHIFT) / float(n)
+    return mean64.astype(np.float32)
+
+
+def smooth_k(k: np.ndarray, km: np.ndarray) -> np.ndarray:
+    """x = fp32(k) - km, in fp32 ([DT] "SageAttention（v1）"); broadcast over tokens."""
+    return k.astype(np.float32) - km[..., None, :].astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# Symmetric absmax INT8 quantiser ([PS] quantisation introduction, steps 1-2)
+# ----------------------------------------------------------------------------
+def quantize_int8_blocks(x: np.ndarray, block: int):
+    """Per-block symmetric INT8 quantisation of fp32 x [..., n, d].
+
+    [PS] quantisation introduction: scale = max|A| / 127, Â = round(A / scale).
+    A block is ``block`` consecutive tokens times all d channels ([DT]
+    "SageAttention（v1）": per-block quantisation of q and k); the last block
+    may be partial.  Division and rounding are fp32 (round half to even);
+    codes are clamped to [-127, 127]; an all-zero block gets scale 0, codes 0.
+
+    Returns (codes int8 [..., n, d], scales fp32 [..., ceil(n/block)]).
+    """
+    if x.dtype != np.float32:
+        raise TypeError("x must be fp32")
+    *lead, n, d = x.shape
+    nb = -(-n // block)
+    pad = nb * block - n
+    xp = x
+    if pad:
+        widths = [(0, 0)] * len(lead) + [(0, pad), (0, 0)]
+        xp = np.pad(x, widths)          # zeros never raise the block max
+    xb = xp.reshape(*lead, nb, block, d)
+    amax = np.abs(xb).max(axis=(-2, -1))                       # fp32, exact
+    scale = (amax / np.float32(INT8_MAX)).astype(np.float32)   # fp32 divide
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    ratio = (xb / safe[..., None, None]).astype(np.float32)    # fp32 divide
+    codes = np.clip(np.rint(ratio), -INT8_MAX, INT8_MAX)
+    codes = np.where((scale > 0)[..., None, None], codes, 0).astype(np.int8)
+    codes = codes.reshape(*lead, nb * block, d)[..., :n, :]
+    return np.ascontiguousarray(codes), scale
+
+
+def quant_q(q: np.ndarray, sm_scale: np.float32):
+    """Q per 128-token block, softmax scale folded into the emitted scale.
+
+    [PS] SageAttention bullets: scaling is fused with the neighbouring
+    operations; here the 1/sqrt(d) of [IP] §2.1 is multiplied (fp32) into δQ
+    after the codes are taken from the unfolded scale.
+    """
+    codes, scale = quantize_int8_blocks(q.astype(np.float32), Q_BLOCK)
+    return codes, (scale * np.float32(sm_scale)).astype(np.float32)
+
+
+def quant_k(k: np.ndarray):
+    """K smoothed by its token mean, then per 64-token block INT8.
+
+    Returns (codes int8, scale fp32 per block, mean fp32 [.., d]).
+    """
+    km = k_token_mean(k)
+    codes, scale = quantize_int8_blocks(smooth_k(k, km), K_BLOCK)
+    return codes, scale, km
+
+
+def quant_qk_dense(q: np.ndarray, k: np.ndarray, sm_scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Dense [B, H, N, d] fp16 inputs ([CS]: HND layout) -> INT8 tensors and scales.
+
+    Output shapes: q_int8, k_int8 [B,H,N,d]; q_scale [B,H,ceil(N/128)];
+    k_scale [B,H,ceil(N/64)]; k_mean [B,H,d].
+    """
+    d = q.shape[-1]
+    sm = default_sm_scale(d) if not sm_scale or sm_scale <= 0 else np.float32(sm_scale)
+    qi, qs = quant_q(q, sm)
+    ki, ks, km = quant_k(k)
+    return dict(q_int8=qi, q_scale=qs, k_int8=ki, k_scale=ks, k_mean=km)
+
+
+def quant_qk_varlen(q: np.ndarray, k: np.ndarray, cu_seqlens: Sequence[int],
+                    sm_scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """Packed [H, T, d] inputs with sequence i on tokens [cu[i], cu[i+1]).
+
+    Blocks and means never cross a sequence.  Scales and means are returned
+    padded per sequence: q_scale [nseq,H,ceil(max/128)], k_scale
+    [nseq,H,ceil(max/64)], k_mean [nseq,H,d]; padding entries are NaN (no
+    value is defined there).
+    """
+    H, T, d = q.shape
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    nseq = len(cu) - 1
+    lens = np.diff(cu)
+    mx = int(lens.max())
+    sm = default_sm_scale(d) if not sm_scale or sm_scale <= 0 else np.float32(sm_scale)
+    qi = np.zeros((H, T, d), np.int8)
+    ki = np.zeros((H, T, d), np.int8)
+    qs = np.full((nseq, H, -(-mx // Q_BLOCK)), np.nan, np.float32)
+    ks = np.full((nseq, H, -(-mx // K_BLOCK)), np.nan, np.float32)
+    km = np.zeros((nseq, H, d), np.float32)
+    for i in range(nseq):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b == a:
+            continue
+        c, s = quant_q(q[:, a:b], sm)
+        qi[:, a:b] = c
+        qs[i, :, : s.shape[-1]] = s
+        c, s, m = quant_k(k[:, a:b])
+        ki[:, a:b] = c
+        ks[i, :, : s.shape[-1]] = s
+        km[i] = m
+    return dict(q_int8=qi, q_scale=qs, k_int8=ki, k_scale=ks, k_mean=km)
+
+
+# ----------------------------------------------------------------------------
+# OCP FP8 E4M3 (e4m3fn) from its definition: 1 sign bit, 4 exponent bits with
+# bias 7, 3 mantissa bits, subnormals at exponent field 0 (spacing 2^-9), the
+# single NaN pattern S.1111.111, largest finite 448.
+# ----------------------------------------------------------------------------
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """e4m3 byte codes -> fp64 values (NaN for the NaN patterns)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(e == 0, np.ldexp(m.astype(np.float64), -9),
+                   np.ldexp((8 + m).astype(np.float64), (e - 10).astype(np.int64)))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Round to the nearest e4m3 value, ties to even mantissa, saturating at ±448."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    neg = np.signbit(np.asarray(x, dtype=np.float64))
+    a = np.minimum(a, E4M3_MAX)
+    # exponent of the leading bit: a = f * 2^E, f in [0.5, 1) -> floor(log2 a) = E - 1
+    _, E = np.frexp(a)
+    e_unb = np.maximum(E - 1, -6)                 # below 2^-6: subnormal spacing 2^-9
+    quantum_exp = e_unb - 3
+    mant = np.rint(np.ldexp(a, -quantum_exp))     # exact scaling by a power of two
+    # mantissa overflow (e.g. 15.5 -> 16) moves to the next binade
+    carry = mant >= 16
+    mant = np.where(carry, mant / 2, mant)
+    e_unb = np.where(carry, e_unb + 1, e_unb)
+    normal = mant >= 8
+    efield = np.where(normal, e_unb + 7, 0)
+    mfield = np.where(normal, mant - 8, mant)
+    code = (efield.astype(np.int64) << 3) | mfield.astype(np.int64)
+    code = np.where(neg, code | 0x80, code)
+    return code.astype(np.uint8)
+
+
+def quant_v_fp8(v: np.ndarray):
+    """V per channel to e4m3 ([DT] "SageAttention 2": P and V in FP8; per-channel
+    V scale = amax over tokens / 448).  v fp16 [..., n, d] ->
+    (codes uint8 [..., n, d], scale fp32 [..., d]).  Division is fp32."""
+    vf = v.astype(np.float32)
+    amax = np.abs(vf).max(axis=-2)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    ratio = (vf / safe[..., None, :]).astype(np.float32)
+    codes = e4m3_encode(ratio)
+    codes = np.where((scale > 0)[..., None, :], codes, np.uint8(0)).astype(np.uint8)
+    return codes, scale
+
+
+def quant_v_fp8_dense(v: np.ndarray):
+    return quant_v_fp8(v)
+
+
+def quant_v_fp8_varlen(v: np.ndarray, cu_seqlens: Sequence[int]):
+    """Packed [H,T,d] -> codes [H,T,d] and scales [nseq,H,d] (per sequence)."""
+    H, T, d = v.shape
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    codes = np.zeros((H, T, d), np.uint8)
+    scales = np.zeros((len(cu) - 1, H, d), np.float32)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            c, s = quant_v_fp8(v[:, a:b])
+            codes[:, a:b] = c
+            scales[i] = s
+    return codes, scales
+
+
+# ----------------------------------------------------------------------------
+# Integer QKᵀ ([PS] SageAttention bullets: QKᵀ in INT8)
+# ----------------------------------------------------------------------------
+def qk_int(q_int8: np.ndarray, k_int8: np.ndarray) -> np.ndarray:
+    """Exact integer Q̂K̂ᵀ: [m, d] x [n, d] -> int64 [m, n].
+
+    Computed as an fp64 matrix product of the small integers; every partial
+    sum is an integer below 2^53, so the result is exact.
+    """
+    r = q_int8.astype(np.float64) @ k_int8.astype(np.float64).T
+    return r.astype(np.int64)
+
+
+# ----------------------------------------------------------------------------
+# The method's attention for selected query rows of one (sequence, head)
+# ----------------------------------------------------------------------------
+def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndarray,
+                        k_scale: np.ndarray, v: np.ndarray, rows: Sequence[int], causal: bool,
+                        pv_mode: str = "fp16", v_scale: Optional[np.ndarray] = None,
+                        tile: int = KV_TILE) -> np.ndarray:
+    """Output rows of the quantised attention for one (sequence, head).
+
+    Inputs: q_int8/k_int8 [n, d] codes, q_scale [ceil(n/128)] (softmax scale
+    folded in), k_scale [ceil(n/64)]; v fp16 [n, d] (fp16 mode) or e4m3 codes
+    [n, d] with v_scale [d] (fp8 mode).  ``rows``: query indices.
+
+    Steps:
+      * S = int(Q̂K̂ᵀ) · δQ · δK  ([PS] quantisation step 3, C ≈ (ÂB̂)(δAδB));
+      * causal: key j > query i is masked ([CS]: is_causal=True);
+      * online softmax over 64-key tiles in ascending order ([IP] §3.1):
+        m' = max(m, max_j s), α = e^(m-m'), p = e^(s-m'), l = αl + Σp;
+      * fp16 mode ([PS] SageAttention bullets, PV in FP16):
+        O = αO + fp16(p)·V, out = fp16(O / l);
+      * fp8 mode ([DT] "SageAttention 2"; [PS] SageAttention2 bullets):
+        level 1: A = e4m3(448 p)·V̂ for this tile alone; level 2: O = αO + A;
+        out = fp16(O · δV / (448 l)).
+    Arithmetic in fp64.  Returns fp16 [len(rows), d].
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    n, d = k_int8.shape
+    R = len(rows)
+    if pv_mode not in ("fp16", "fp8"):
+        raise ValueError(pv_mode)
+    qf = q_int8[rows].astype(np.float64)
+    dq = q_scale[rows // Q_BLOCK].astype(np.float64)
+    if pv_mode == "fp8":
+        if v_scale is None:
+            raise ValueError("fp8 mode needs v_scale")
+        vv = e4m3_decode(v)
+    else:
+        vv = v.astype(np.float64)
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    O = np.zeros((R, d))
+    last_row = int(rows.max()) if R else -1
+    with np.errstate(invalid="ignore", over="ignore"):
+        for t0 in range(0, n, tile):
+            if causal and t0 > last_row:
+                break                                   # no visible key for any row
+            keys = np.arange(t0, min(n, t0 + tile))
+            acc = qf @ k_int8[keys].astype(np.float64).T
+            dk = k_scale[keys // K_BLOCK].astype(np.float64)
+            s = acc * dq[:, None] * dk[None, :]
+            if causal:
+                s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+            m_new = np.maximum(m, s.max(axis=1))
+            live = m_new > -np.inf
+            alpha = np.where(live, np.exp(m - m_new), 1.0)
+            alpha = np.where(np.isneginf(m) & live, 0.0, alpha)
+            p = np.where(live[:, None], np.exp(s - m_new[:, None]), 0.0)
+            l = alpha * l + p.sum(axis=1)
+            if pv_mode == "fp16":
+                pq = p.astype(np.float16).astype(np.float64)
+                O = alpha[:, None] * O + pq @ vv[keys]
+            else:
+                pq = e4m3_decode(e4m3_encode(p * E4M3_MAX))
+                A = pq @ vv[keys]                       # level 1: this tile only
+                O = alpha[:, None] * O + A              # level 2: running output
+            m = m_new
+    if pv_mode == "fp16":
+        out = O / l[:, None]
+    else:
+        out = O * v_scale.astype(np.float64)[None, :] / (E4M3_MAX * l[:, None])
+    return out.astype(np.float16)
+
+
+# ----------------------------------------------------------------------------
+# Plain definition: fp64 scaled-dot-product attention ([IP] §2.1)
+# ----------------------------------------------------------------------------
+def sdpa_fp64_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: Sequence[int],
+                   causal: bool, sm_scale: Optional[float] = None) -> np.ndarray:
+    """softmax(q kᵀ · sm_scale) v for the given query rows, in fp64, no
+    quantisation and no smoothing.  q, k, v [n, d] (any float dtype)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    n, d = k.shape
+    scale = 1.0 / math.sqrt(d) if sm_scale is None else float(sm_scale)
+    s = (q[rows].astype(np.float64) @ k.astype(np.float64).T) * scale
+    if causal:
+        s = np.where(np.arange(n)[None, :] > rows[:, None], -np.inf, s)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ v.astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# Convenience views: one (sequence, head) slice of the ABI-layout arrays
+# ----------------------------------------------------------------------------
+def head_views_dense(quant: Dict[str, np.ndarray], b: int, h: int):
+    return (quant["q_int8"][b, h], quant["q_scale"][b, h], quant["k_int8"][b, h],
+            quant["k_scale"][b, h])
+
+
+def head_views_varlen(quant: Dict[str, np.ndarray], cu_seqlens, i: int, h: int):
+    a, b = int(cu_seqlens[i]), int(cu_seqlens[i + 1])
+    n = b - a
+    return (quant["q_int8"][h, a:b], quant["q_scale"][i, h, : -(-n // Q_BLOCK)],
+            quant["k_int8"][h, a:b], quant["k_scale"][i, h, : -(-n // K_BLOCK)])

@@ -1,0 +1,381 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself
+(the pages' worked example, brute force, exact rationals, closed forms,
+library routines, invariants and special cases).  CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import sage_oracle as O
+import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def cos(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def fraction_to_f32(fr: Fraction) -> np.float32:
+    """Correctly rounded (ties to even) fp32 of an exact rational, by search."""
+    c = np.float32(float(fr))
+    best = None
+    for cand in (np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))):
+        dist = abs(Fraction(float(cand)) - fr)
+        key = (dist, int(np.array(cand).view(np.uint32)) & 1)
+        if best is None or key < best[0]:
+            best = (key, cand)
+    return best[1]
+
+
+# --------------------------------------------------------------------------
+# Quantiser
+# --------------------------------------------------------------------------
+def test_worked_example_from_page():
+    g = json.load(open(os.path.join(GOLDEN, "quant_worked_example.json")))
+    a = np.array(g["input"], np.float16).astype(np.float32).reshape(1, -1)   # 1 token x 4 channels
+    codes, scale = O.quantize_int8_blocks(a, block=1)
+    assert codes.ravel().tolist() == g["codes"]
+    assert round(float(scale[0]), g["scale_printed_decimals"]) == pytest.approx(g["scale_printed"])
+    assert scale[0] == np.float32(np.float32(1000.0) / np.float32(127.0))
+
+
+@pytest.mark.parametrize("block", [1, 3, 64, 128])
+def test_quantizer_brute_force(block):
+    rng = np.random.default_rng(11)
+    n, d = 2 * block + 5, 8                      # several blocks and a partial one
+    x = (rng.standard_normal((n, d)) * rng.choice([0.01, 1.0, 50.0], size=(n, 1))).astype(np.float32)
+    codes, scale = O.quantize_int8_blocks(x, block)
+    nb = -(-n // block)
+    assert scale.shape == (nb,)
+    cand = np.arange(-127, 128)
+    for b in range(nb):
+        xb = x[b * block:(b + 1) * block]
+        amax = max(abs(float(v)) for v in xb.ravel())
+        assert scale[b] == np.float32(np.float32(amax) / np.float32(127))
+        for (i, j), v in np.ndenumerate(xb):
+            r = float(np.float32(np.float32(v) / scale[b]))
+            dist = np.abs(r - cand)
+            best = cand[dist == dist.min()]
+            want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+            assert codes[b * block + i, j] == want
+
+
+def test_quantizer_error_bound_and_full_range():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((1000, 64)) * 3).astype(np.float32)
+    codes, scale = O.quantize_int8_blocks(x, 64)
+    blk = np.arange(1000) // 64
+    deq = codes.astype(np.float64) * scale[blk][:, None].astype(np.float64)
+    err = np.abs(x.astype(np.float64) - deq)
+    bound = scale[blk].astype(np.float64)[:, None] * (0.5 + 2.0 ** -22)
+    assert (err <= bound).all()
+    for b in range(len(scale)):
+        assert np.abs(codes[blk == b]).max() == 127
+
+
+def test_quantizer_zero_block():
+    x = np.zeros((130, 16), np.float32)
+    x[64:128] = 1.5
+    codes, scale = O.quantize_int8_blocks(x, 64)
+    assert scale[0] == 0 and scale[2] == 0 and scale[1] > 0
+    assert (codes[:64] == 0).all() and (codes[128:] == 0).all()
+    assert (codes[64:128] == 127).all()
+
+
+def test_q_scale_folds_softmax_scale():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 1, 300, 64)).astype(np.float16)
+    codes, s = O.quant_q(q, O.default_sm_scale(64))
+    codes2, s2 = O.quantize_int8_blocks(q.astype(np.float32), 128)
+    assert (codes == codes2).all()
+    assert (s == (s2 * np.float32(0.125)).astype(np.float32)).all()
+    assert O.default_sm_scale(128) == np.float32(1 / math.sqrt(128))
+
+
+# --------------------------------------------------------------------------
+# K mean and smoothing
+# --------------------------------------------------------------------------
+def test_k_mean_exact_rational():
+    rng = np.random.default_rng(7)
+    for n in (1, 2, 3, 37, 64):
+        k = (rng.standard_normal((n, 6)) * rng.choice([1e-3, 1.0, 300.0])).astype(np.float16)
+        km = O.k_token_mean(k)
+        for c in range(6):
+            exact = sum(Fraction(float(v)) for v in k[:, c]) / n
+            assert km[c] == fraction_to_f32(exact), (n, c)
+
+
+def test_k_mean_order_independent_and_smoothing_centres():
+    rng = np.random.default_rng(8)
+    k = (rng.standard_normal((500, 32)) + rng.standard_normal(32) * 5).astype(np.float16)
+    km = O.k_token_mean(k)
+    perm = rng.permutation(500)
+    assert (O.k_token_mean(k[perm]).view(np.uint32) == km.view(np.uint32)).all()
+    x = O.smooth_k(k, km)
+    colmean = x.astype(np.float64).mean(axis=0)
+    assert np.abs(colmean).max() < 1e-5 * (1 + np.abs(km).max())
+    assert np.abs(km - k.astype(np.float64).mean(axis=0)).max() < 1e-6 * (1 + np.abs(km).max())
+
+
+def test_smoothing_leaves_exact_attention_unchanged():
+    rng = np.random.default_rng(9)
+    n, d = 200, 64
+    q = rng.standard_normal((n, d)).astype(np.float16)
+    k = (rng.standard_normal((n, d)) + 3 * rng.standard_normal(d)).astype(np.float16)
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    km = O.k_token_mean(k).astype(np.float64)
+    rows = np.arange(n)
+    for causal in (False, True):
+        a = O.sdpa_fp64_rows(q, k, v, rows, causal)
+        b = O.sdpa_fp64_rows(q, k.astype(np.float64) - km, v, rows, causal)
+        assert np.abs(a - b).max() <= 1e-9 * np.abs(a).max()
+
+
+# --------------------------------------------------------------------------
+# e4m3
+# --------------------------------------------------------------------------
+def test_e4m3_decode_table():
+    dec = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert dec[0x7E] == 448.0 and dec[0x38] == 1.0 and dec[0x08] == 2.0 ** -6
+    assert dec[0x01] == 2.0 ** -9 and dec[0x07] == 7 * 2.0 ** -9
+    assert np.isnan(dec[0x7F]) and np.isnan(dec[0xFF])
+    assert dec[0xFE] == -448.0
+    finite = ~np.isnan(dec)
+    assert finite.sum() == 254
+    pos = np.sort(dec[:0x7F])
+    assert (np.diff(pos) > 0).all()      # 127 distinct non-negative values
+
+
+def test_e4m3_roundtrip_and_ties():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    assert (O.e4m3_encode(O.e4m3_decode(codes)) == codes).all()
+    # midpoints between neighbours go to the even mantissa
+    vals = O.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (vals[:-1] + vals[1:]) / 2
+    enc = O.e4m3_encode(mids)
+    assert ((enc & 1) == 0).all()
+    assert (np.abs(O.e4m3_decode(enc) - mids) == (vals[1:] - vals[:-1]) / 2).all()
+    # saturation
+    assert O.e4m3_encode(np.array([460.0, 1e6, -500.0])).tolist() == [0x7E, 0x7E, 0xFE]
+
+
+def test_e4m3_matches_torch_cast():
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal(200000) * np.exp2(rng.integers(-12, 9, 200000))).astype(np.float32)
+    x = np.clip(x, -448, 448)
+    ours = O.e4m3_encode(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert (ours == ref).all()
+
+
+def test_quant_v_fp8_brute_force():
+    rng = np.random.default_rng(4)
+    v = (rng.standard_normal((2, 77, 8)) * rng.choice([0.1, 4.0], size=(2, 1, 8))).astype(np.float16)
+    v[1, :, 3] = 0
+    codes, scale = O.quant_v_fp8(v)
+    assert scale.shape == (2, 8)
+    for h in range(2):
+        for c in range(8):
+            col = v[h, :, c].astype(np.float32)
+            s = np.float32(np.abs(col).max()) / np.float32(448)
+            assert scale[h, c] == s
+            if s == 0:
+                assert (codes[h, :, c] == 0).all()
+                continue
+            ratio = (col / s).astype(np.float32)
+            want = torch.from_numpy(np.clip(ratio, -448, 448)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert (codes[h, :, c] == want).all()
+
+
+# --------------------------------------------------------------------------
+# Integer QKᵀ and the fp64 definition
+# --------------------------------------------------------------------------
+def test_qk_int_two_ways():
+    rng = np.random.default_rng(2)
+    a = rng.integers(-127, 128, (128, 128)).astype(np.int8)
+    b = rng.integers(-127, 128, (64, 128)).astype(np.int8)
+    ref = np.einsum("ic,jc->ij", a.astype(np.int64), b.astype(np.int64))
+    assert (O.qk_int(a, b) == ref).all()
+    full = np.full((4, 128), 127, np.int8)
+    assert (O.qk_int(full, -full) == -128 * 127 * 127).all()
+
+
+def test_sdpa_fp64_against_torch_and_loops():
+    rng = np.random.default_rng(6)
+    n, d = 70, 16
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    for causal in (False, True):
+        ours = O.sdpa_fp64_rows(q, k, v, np.arange(n), causal)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+            is_causal=causal).numpy()[0]
+        assert np.abs(ours - ref).max() < 1e-12
+    # pure-python loops on a tiny case
+    n, d = 5, 3
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    ours = O.sdpa_fp64_rows(q, k, v, np.arange(n), True)
+    for i in range(n):
+        s = [sum(q[i][c] * k[j][c] for c in range(d)) / math.sqrt(d) for j in range(i + 1)]
+        mx = max(s)
+        e = [math.exp(x - mx) for x in s]
+        tot = sum(e)
+        for c in range(d):
+            assert abs(ours[i][c] - sum(e[j] * v[j][c] for j in range(i + 1)) / tot) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# The method's attention: special cases, lossless grid, tiling, accuracy
+# --------------------------------------------------------------------------
+def _run(q, k, v, causal, pv_mode="fp16", rows=None, tile=O.KV_TILE):
+    quant = O.quant_qk_dense(q[None, None], k[None, None])
+    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+    n = q.shape[0]
+    rows = np.arange(n) if rows is None else rows
+    if pv_mode == "fp8":
+        vc, vs = O.quant_v_fp8(v)
+        return O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs, tile=tile)
+    return O.sage_attention_rows(qi, qs, ki, ks, v, rows, causal, "fp16", tile=tile)
+
+
+def test_single_token_returns_v():
+    rng = np.random.default_rng(12)
+    for d in (64, 128):
+        q, k, v = (rng.standard_normal((1, d)).astype(np.float16) for _ in range(3))
+        assert (_run(q, k, v, False).view(np.uint16) == v.view(np.uint16)).all()
+        vc, vs = O.quant_v_fp8(v)
+        want = (O.e4m3_decode(vc) * vs.astype(np.float64)).astype(np.float16)
+        assert (_run(q, k, v, False, "fp8").view(np.uint16) == want.view(np.uint16)).all()
+
+
+def test_causal_first_row_returns_v0():
+    rng = np.random.default_rng(13)
+    q, k, v = (rng.standard_normal((150, 64)).astype(np.float16) for _ in range(3))
+    out = _run(q, k, v, True, rows=np.array([0, 1, 149]))
+    assert (out[0].view(np.uint16) == v[0].view(np.uint16)).all()
+    assert not (out[1].view(np.uint16) == v[0].view(np.uint16)).all()
+
+
+def test_zero_query_gives_mean_of_visible_values():
+    rng = np.random.default_rng(14)
+    n, d = 200, 64
+    q = np.zeros((n, d), np.float16)
+    k, v = (rng.standard_normal((n, d)).astype(np.float16) for _ in range(2))
+    out = _run(q, k, v, False)
+    want = v.astype(np.float64).mean(axis=0).astype(np.float16)
+    assert (out.view(np.uint16) == want[None].view(np.uint16)).all()
+    outc = _run(q, k, v, True, rows=np.array([0, 63, 64, 199]))
+    for r, i in enumerate([0, 63, 64, 199]):
+        want = v[: i + 1].astype(np.float64).mean(axis=0).astype(np.float16)
+        assert (outc[r].view(np.uint16) == want.view(np.uint16)).all()
+
+
+def test_lossless_grid_matches_exact_attention():
+    rng = np.random.default_rng(15)
+    n, d = 320, 64
+    q = np.zeros((n, d))
+    for b in range(3):
+        step = 2.0 ** -(4 + b)
+        blk = rng.integers(-127, 128, (min(128, n - 128 * b), d)).astype(np.float64)
+        blk[0, 0] = 127
+        q[128 * b:128 * b + len(blk)] = blk * step
+    # K: 5 blocks of 64 with steps differing per block; column sums exactly zero
+    # (each block is paired with a mirrored block of the same step).
+    steps = [2.0 ** -3, 2.0 ** -5, 2.0 ** -5, 2.0 ** -3, 2.0 ** -4]
+    k = np.zeros((n, d))
+    base = rng.integers(-126, 127, (64, d)).astype(np.float64)
+    base[0, 0] = 127
+    base2 = rng.integers(-126, 127, (64, d)).astype(np.float64)
+    base2[1, 1] = -127
+    k[0:64] = base * steps[0]
+    k[192:256] = -base * steps[3]
+    k[64:128] = base2 * steps[1]
+    k[128:192] = -base2 * steps[2]
+    base3 = rng.integers(-126, 127, (32, d)).astype(np.float64)
+    base3[0, 2] = 127
+    k[256:288] = base3 * steps[4]
+    k[288:320] = -base3 * steps[4]
+    q16, k16 = q.astype(np.float16), k.astype(np.float16)
+    assert (q16.astype(np.float64) == q).all() and (k16.astype(np.float64) == k).all()
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    quant = O.quant_qk_dense(q16[None, None], k16[None, None])
+    assert (quant["k_mean"] == 0).all()
+    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+    # codes reproduce the inputs exactly, with the per-block scales
+    assert (qi.astype(np.float64) * (qs[np.arange(n) // 128] / np.float32(0.125)).astype(np.float64)[:, None] == q).all()
+    assert (ki.astype(np.float64) * ks[np.arange(n) // 64].astype(np.float64)[:, None] == k).all()
+    assert ks.tolist() == steps
+    for causal in (False, True):
+        ours = O.sage_attention_rows(qi, qs, ki, ks, v, np.arange(n), causal)
+        ref = O.sdpa_fp64_rows(q16, k16, v, np.arange(n), causal)
+        assert cos(ours, ref) >= 0.99999
+        assert np.abs(ours - ref).max() < 4e-3
+
+
+def test_tile_schedule_does_not_matter_in_fp16_mode():
+    rng = np.random.default_rng(16)
+    n, d = 300, 64
+    q, v = (rng.standard_normal((n, d)).astype(np.float16) for _ in range(2))
+    k = (rng.standard_normal((n, d)) + 3 * rng.standard_normal(d)).astype(np.float16)
+    for causal in (False, True):
+        a = _run(q, k, v, causal, tile=64)
+        b = _run(q, k, v, causal, tile=n)
+        assert cos(a, b) >= 0.99999
+        assert np.abs(a.astype(np.float64) - b).max() < 2e-3
+
+
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_method_close_to_exact_attention(pv_mode, causal):
+    """The pages' per-layer bar of 99.8 % cosine ([DT] "SageAttention（v1）")."""
+    x = workloads.generate_custom(31, 1, 2, 1000, 128, k_bias=3.0, q_bias=3.0 if pv_mode == "fp8" else 0.0)
+    for h in range(2):
+        q, k, v = x.q[0, h], x.k[0, h], x.v[0, h]
+        ours = _run(q, k, v, causal, pv_mode)
+        ref = O.sdpa_fp64_rows(q, k, v, np.arange(1000), causal)
+        assert cos(ours, ref) >= 0.998
+
+
+def test_fp8_two_level_accumulation_equals_single_sum():
+    """Level 1 (one tile) then level 2 (running output) equals the plain sum when
+    the max never changes: with all scores equal, every p is 1."""
+    rng = np.random.default_rng(17)
+    n, d = 256, 64
+    q = np.zeros((n, d), np.float16)
+    k = rng.standard_normal((n, d)).astype(np.float16)
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    vc, vs = O.quant_v_fp8(v)
+    out = _run(q, k, v, False, "fp8", rows=np.array([5]))
+    want = (O.e4m3_decode(vc).sum(axis=0) * 448 * vs.astype(np.float64) / (448 * n)).astype(np.float16)
+    assert (out[0].view(np.uint16) == want.view(np.uint16)).all()
+
+
+def test_varlen_equals_per_sequence_dense():
+    x = workloads.generate_custom(41, 0, 2, 0, 64, lengths=[1, 70, 200])
+    cu = x.cu_seqlens
+    quant = O.quant_qk_varlen(x.q, x.k, cu)
+    for i in range(3):
+        a, b = cu[i], cu[i + 1]
+        dense = O.quant_qk_dense(x.q[:, a:b][None], x.k[:, a:b][None])
+        assert (quant["q_int8"][:, a:b] == dense["q_int8"][0]).all()
+        assert (quant["k_int8"][:, a:b] == dense["k_int8"][0]).all()
+        assert (quant["k_mean"][i] == dense["k_mean"][0]).all()
+        nq, nk = dense["q_scale"].shape[-1], dense["k_scale"].shape[-1]
+        assert (quant["q_scale"][i, :, :nq] == dense["q_scale"][0]).all()
+        assert (quant["k_scale"][i, :, :nk] == dense["k_scale"][0]).all()
+
+
+def test_workload_recipe_shapes():
+    w = workloads.get("tiny")
+    x = workloads.generate(w)
+    assert x.q.shape == (1, 2, 256, 64) and x.q.dtype == np.float16
+    assert np.abs(x.k.astype(np.float64).mean(axis=2)).mean() > 1.0     # the K bias is there
+    wv = workloads.get("varlen")
+    lens = workloads.sequence_lengths(wv)
+    assert len(lens) == 16 and lens.min() >= 512 and lens.max() <= 8192
