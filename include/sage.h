@@ -1,0 +1,184 @@
+/*
+ * sage.h — C ABI of the MI355X (gfx950) 8-bit quantised attention forward.
+ *
+ * What is computed (pages cited by title and section):
+ *   - K smoothing: K minus its per-channel token mean, which leaves softmax
+ *     unchanged (dtcms.com SageAttention summary, section "SageAttention（v1）";
+ *     "⚡️SageAttention — brand new attention", SageAttention bullets).
+ *   - Per-block symmetric INT8 quantisation of Q (128-token blocks) and of the
+ *     smoothed K (64-token blocks): scale = max|x|/127, code = round(x/scale)
+ *     ("⚡️SageAttention — brand new attention", quantisation introduction;
+ *     dtcms summary "SageAttention（v1）", per-block quantisation).  The softmax
+ *     scale is folded into Q's scale (same page, "fuse scaling and unscaling").
+ *   - A tiled, fused attention (intelliparadigm "Attention机制优化", §3.1:
+ *     tiling, fusion, online softmax): S = int32(Q̂K̂ᵀ)·δQ·δK, online fp32
+ *     softmax, PV in FP16 with fp32 accumulation, or FP8 (e4m3) PV with
+ *     per-channel V scales and two-level accumulation (dtcms summary, section
+ *     "SageAttention 2"; postsniper page, SageAttention2 bullets).
+ *   - Causal masking and variable-length packed batches (deepseek.csdn.net
+ *     post: sageattn called with is_causal=True on [B,H,N,d] tensors;
+ *     jsqmd "SageAttention完全指南", API list: sageattn_varlen).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers (HIP global memory) unless stated.
+ *     fp16 is IEEE binary16; the last dimension (d) is contiguous.
+ *   - Layout HND: dense tensors are [B, H, N, d]; varlen tensors are packed
+ *     [H, T, d] with sequence i on tokens [cu_seqlens[i], cu_seqlens[i+1]).
+ *   - Supported head dims: d = 64 or d = 128.
+ *   - Ownership: the caller allocates and frees every buffer, the workspace
+ *     included.  The library never allocates or frees device memory and keeps
+ *     no pointer after a call returns.
+ *   - Asynchrony: calls only enqueue work on `stream` (a hipStream_t; NULL is
+ *     the null stream) and return without synchronising.  Buffers must stay
+ *     valid until the stream has completed the work.
+ *   - Errors: all validation happens on the host before anything is enqueued;
+ *     on an error nothing is launched and outputs are untouched.  Null or
+ *     misaligned (not 16-byte aligned) pointers, non-positive sizes, d not in
+ *     {64,128}, unknown enum values -> SAGE_ERR_INVALID_ARGUMENT; a layout the
+ *     library does not implement -> SAGE_ERR_UNSUPPORTED; a workspace smaller
+ *     than the size query -> SAGE_ERR_WORKSPACE_TOO_SMALL; a failed launch ->
+ *     SAGE_ERR_DEVICE.  No C++ exception crosses this boundary.
+ *   - Inputs must be finite; the contents of cu_seqlens must satisfy the
+ *     documented constraints (they live on the device and are not checked).
+ *   - Calls are reentrant; the library holds no mutable global state.
+ */
+#ifndef SAGE_H_
+#define SAGE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARGUMENT = 1,
+  SAGE_ERR_UNSUPPORTED = 2,
+  SAGE_ERR_WORKSPACE_TOO_SMALL = 3,
+  SAGE_ERR_DEVICE = 4
+} sage_status_t;
+
+typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1 } sage_pv_mode_t;
+typedef enum { SAGE_LAYOUT_HND = 0 } sage_layout_t;
+
+/* A hipStream_t passed as an opaque pointer. */
+typedef void* sage_stream_t;
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char* sage_status_string(sage_status_t s);
+
+/* ------------------------------------------------------------------------
+ * sage_quant_qk — K smoothing + per-block INT8 quantisation of Q and K.
+ *   (postsniper page, quantisation introduction and SageAttention bullets;
+ *    dtcms summary, section "SageAttention（v1）")
+ *
+ * cu_seqlens == NULL: dense. q, k fp16 [B,H,N,d]; outputs q_int8, k_int8
+ *   int8 [B,H,N,d]; q_scale fp32 [B,H,ceil(N/128)]; k_scale fp32
+ *   [B,H,ceil(N/64)]; k_mean fp32 [B,H,d].  total_tokens is ignored.
+ * cu_seqlens != NULL: varlen.  B = number of sequences, N = max sequence
+ *   length (>= every length), total_tokens = T = cu_seqlens[B].  q, k, q_int8,
+ *   k_int8 are packed [H,T,d]; q_scale [B,H,ceil(N/128)], k_scale
+ *   [B,H,ceil(N/64)] and k_mean [B,H,d] are indexed by sequence, entries past
+ *   a sequence's own block count are left unwritten.  cu_seqlens is int32
+ *   [B+1] on the device, cu[0]=0, non-decreasing, cu[B]=T, each length <= N.
+ * sm_scale <= 0 selects the default fp32(1/sqrt(d)).  q_scale holds the block
+ *   scale times sm_scale (fp32 product).
+ * Semantics (bit-exact contract): km = fp32(exact int64 fixed-point column sum
+ *   * 2^-24 / n) per (sequence, head, channel); x = fp32(k) - km in fp32;
+ *   scale = fp32(max|x| / 127) (IEEE division); code = clamp(rint(fp32(x /
+ *   scale)), -127, 127); an all-zero block has scale 0 and codes 0.  Q the same
+ *   without the mean.
+ * workspace: device scratch of at least sage_quant_qk_workspace_size(B,H,d)
+ *   bytes, 256-byte aligned; its contents on entry do not matter.
+ */
+size_t sage_quant_qk_workspace_size(int B, int H, int d);
+sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d,
+                            sage_layout_t layout, const int32_t* cu_seqlens, int64_t total_tokens,
+                            float sm_scale, int8_t* q_int8, int8_t* k_int8, float* q_scale,
+                            float* k_scale, float* k_mean, void* workspace, size_t workspace_bytes,
+                            sage_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sage_quant_v_fp8 — per-channel e4m3 quantisation of V (the FP8-PV input).
+ *   (dtcms summary, section "SageAttention 2": P and V in FP8)
+ * Dense (cu_seqlens == NULL): v fp16 [B,H,N,d] -> v_fp8 e4m3 bytes [B,H,N,d],
+ *   v_scale fp32 [B,H,d].  Varlen: v, v_fp8 packed [H,T,d], v_scale [B,H,d]
+ *   per sequence.  scale = fp32(max_t |v| / 448); code = e4m3 of
+ *   fp32(v / scale), round to nearest even, saturating at ±448 (OCP E4M3FN);
+ *   a zero channel has scale 0 and codes 0.  No workspace.
+ */
+sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_layout_t layout,
+                               const int32_t* cu_seqlens, int64_t total_tokens, uint8_t* v_fp8,
+                               float* v_scale, sage_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sage_attn_fwd — full forward on dense [B,H,N,d] fp16 tensors.
+ *   q, k, v inputs; o output fp16 [B,H,N,d] (may not alias the inputs).
+ *   is_causal != 0 masks key j > query i (deepseek.csdn.net post: is_causal).
+ *   pv_mode selects FP16 PV or FP8-e4m3 PV.  sm_scale <= 0 -> 1/sqrt(d).
+ *   The pre-pass (smoothing, quantisation, V packing) writes into the
+ *   caller's workspace of at least sage_attn_workspace_size(...) bytes; its
+ *   layout is internal (see sage_test_workspace_layout).
+ */
+size_t sage_attn_workspace_size(int B, int H, int N, int d, sage_pv_mode_t pv_mode);
+sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
+                            int N, int d, sage_layout_t layout, int is_causal,
+                            sage_pv_mode_t pv_mode, float sm_scale, void* workspace,
+                            size_t workspace_bytes, sage_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sage_attn_varlen_fwd — forward on packed variable-length sequences.
+ *   (jsqmd "SageAttention完全指南", API list: sageattn_varlen)
+ *   q, k, v, o packed fp16 [H,T,d]; cu_seqlens device int32 [nseq+1] with
+ *   cu[0]=0, non-decreasing, cu[nseq]=total_tokens, every length <=
+ *   max_seqlen.  Means, quantisation blocks and the causal mask are per
+ *   sequence.  Empty sequences are allowed.
+ */
+size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H, int d,
+                                       sage_pv_mode_t pv_mode);
+sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o,
+                                   const int32_t* cu_seqlens, int nseq, int max_seqlen,
+                                   int64_t total_tokens, int H, int d, int is_causal,
+                                   sage_pv_mode_t pv_mode, float sm_scale, void* workspace,
+                                   size_t workspace_bytes, sage_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Test hooks (stable; prefix sage_test_).
+ *
+ * sage_test_workspace_layout: byte offsets, inside the sage_attn_fwd
+ *   (varlen == 0) or sage_attn_varlen_fwd (varlen != 0) workspace, of
+ *   [0] q_int8, [1] k_int8, [2] q_scale, [3] k_scale, [4] k_mean,
+ *   [5] packed V, [6] v_scale (fp8 mode; an empty region in fp16 mode),
+ *   [7] total size (internal scratch sits between [6] and [7]).
+ *   For dense calls pass B,H,N,d (nseq,total_tokens ignored); for varlen pass
+ *   B = nseq, N = max_seqlen and total_tokens.  offsets_out is HOST memory.
+ *   The int8/scale/mean regions use the same layouts as sage_quant_qk.
+ *
+ * sage_test_qk_tiles: int32 tiles of Q̂K̂ᵀ (128 queries x 64 keys each, row =
+ *   query) for a list of (b, h, q_block, k_block) quadruples (device int32
+ *   [n,4]) on dense int8 [B,H,N,d] inputs, computed by the attention kernel's
+ *   own QKᵀ device code; entries outside [0,N) read as zero codes.  out is
+ *   device int32 [n,128,64].
+ */
+/*
+ * sage_test_attn_from_workspace: launch only the fused attention kernel on a
+ *   workspace that a preceding sage_attn_fwd call with the same B,H,N,d,
+ *   is_causal and pv_mode has filled (its pre-pass results are reused as they
+ *   are); writes o fp16 [B,H,N,d].  Used to time the attention kernel alone.
+ *   Same validation as sage_attn_fwd.
+ */
+sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int N, int d, int is_causal,
+                                            sage_pv_mode_t pv_mode, const void* workspace,
+                                            size_t workspace_bytes, sage_stream_t stream);
+sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int N, int64_t total_tokens,
+                                         int d, sage_pv_mode_t pv_mode, size_t offsets_out[8]);
+sage_status_t sage_test_qk_tiles(const int8_t* q_int8, const int8_t* k_int8, int B, int H, int N,
+                                 int d, const int32_t* tile_list, int n_tiles, int32_t* out,
+                                 sage_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_H_ */

@@ -1,0 +1,297 @@
+// C ABI of the 8-bit attention forward (declarations and contracts in
+// include/sage.h).  Every argument is validated on the host before anything
+// is enqueued; on error nothing is launched.
+#include "sage.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+
+#include "sage_internal.h"
+
+namespace {
+
+using sage::ceil_div64;
+using sage::SeqGeom;
+
+constexpr size_t kWsAlign = 256;
+constexpr int64_t kMaxTokensPerSeq = int64_t(1) << 23;  // keeps the int64 fixed-point K sums exact
+
+inline size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool debug_sync() {
+  static const bool on = [] {
+    const char* e = std::getenv("SAGE_DEBUG");
+    return e && e[0] == '1';
+  }();
+  return on;
+}
+
+// Offsets inside the attention workspace:
+// [0] q_int8 [1] k_int8 [2] q_scale [3] k_scale [4] k_mean [5] packed V
+// [6] v_scale (fp8) [7] int64 K column sums; total returned separately.
+struct WsLayout {
+  size_t off[8];
+  size_t total;
+};
+
+WsLayout make_layout(bool varlen, int B, int H, int N, int64_t T, int d, bool fp8) {
+  const int64_t tokens = varlen ? (int64_t)H * T : (int64_t)B * H * N;
+  const int64_t E = tokens * d;
+  const int64_t nqb = ceil_div64(N, sage::kQBlock), nkb = ceil_div64(N, sage::kKBlock);
+  const int64_t vtiles = varlen ? (int64_t)H * sage::vtiles_per_head_varlen(T, B) : (int64_t)B * H * nkb;
+  const size_t sizes[8] = {
+      (size_t)E,
+      (size_t)E,
+      sizeof(float) * (size_t)B * H * nqb,
+      sizeof(float) * (size_t)B * H * nkb,
+      sizeof(float) * (size_t)B * H * d,
+      (size_t)vtiles * sage::kKBlock * d * (fp8 ? 1 : 2),
+      fp8 ? sizeof(float) * (size_t)B * H * d : 0,
+      sizeof(long long) * (size_t)B * H * d,
+  };
+  WsLayout L;
+  size_t cur = 0;
+  for (int i = 0; i < 8; ++i) {
+    L.off[i] = cur;
+    cur = align_up(cur + sizes[i]);
+  }
+  L.total = cur;
+  return L;
+}
+
+sage_status_t check_dims(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return SAGE_ERR_INVALID_ARGUMENT;
+  if (B > 65535 || H > 65535 || N > kMaxTokensPerSeq) return SAGE_ERR_INVALID_ARGUMENT;
+  const int64_t blocks = (int64_t)B * H * ceil_div64(N, sage::kQBlock);
+  if (blocks > 0x7fffffffLL) return SAGE_ERR_INVALID_ARGUMENT;
+  return SAGE_OK;
+}
+
+bool resolve_sm_scale(float in, int d, float* out) {
+  if (std::isnan(in) || std::isinf(in)) return false;
+  *out = in > 0.f ? in : (float)(1.0 / std::sqrt((double)d));
+  return true;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+sage_status_t finish(hipStream_t st) {
+  if (hipGetLastError() != hipSuccess) return SAGE_ERR_DEVICE;
+  if (debug_sync()) {
+    const hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) {
+      std::fprintf(stderr, "sage: device error %s\n", hipGetErrorString(e));
+      return SAGE_ERR_DEVICE;
+    }
+  }
+  return SAGE_OK;
+}
+
+// Shared body of the dense and varlen forward.
+sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o, const SeqGeom& g, bool varlen,
+                           int is_causal, sage_pv_mode_t pv_mode, float sm_scale, void* workspace,
+                           size_t workspace_bytes, sage_stream_t stream) noexcept {
+  if (!q || !k || !v || !o || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAGE_ERR_INVALID_ARGUMENT;
+  if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  float sm;
+  if (!resolve_sm_scale(sm_scale, g.d, &sm)) return SAGE_ERR_INVALID_ARGUMENT;
+  const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
+  const WsLayout L = make_layout(varlen, g.B, g.H, g.N, g.T, g.d, fp8);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
+  const size_t tensor_bytes = (size_t)(varlen ? (int64_t)g.H * g.T : (int64_t)g.B * g.H * g.N) * g.d * 2;
+  if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
+      overlaps(o, tensor_bytes, v, tensor_bytes) || overlaps(o, tensor_bytes, workspace, L.total))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (tensor_bytes == 0) return SAGE_OK;  // varlen with no tokens at all
+
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int8_t* q8 = reinterpret_cast<int8_t*>(ws + L.off[0]);
+  int8_t* k8 = reinterpret_cast<int8_t*>(ws + L.off[1]);
+  float* qs = reinterpret_cast<float*>(ws + L.off[2]);
+  float* ks = reinterpret_cast<float*>(ws + L.off[3]);
+  float* km = reinterpret_cast<float*>(ws + L.off[4]);
+  uint8_t* vp = reinterpret_cast<uint8_t*>(ws + L.off[5]);
+  float* vs = reinterpret_cast<float*>(ws + L.off[6]);
+  long long* colsum = reinterpret_cast<long long*>(ws + L.off[7]);
+
+  sage::launch_quant_qk(g, q, k, sm, q8, k8, qs, ks, km, colsum, st);
+  if (fp8) sage::launch_v_scale(g, v, vs, st);
+  sage::launch_v_prepare(g, v, vs, fp8, /*rowmajor=*/false, vp, st);
+  sage::AttnArgs a{q8, k8, qs, ks, vp, vs, static_cast<uint16_t*>(o), g};
+  sage::launch_attn(a, is_causal != 0, fp8, st);
+  return finish(st);
+}
+
+sage_status_t varlen_geom(const int32_t* cu, int nseq, int max_seqlen, int64_t total_tokens, int H, int d,
+                          SeqGeom* g) {
+  if (!cu) return SAGE_ERR_INVALID_ARGUMENT;
+  if (nseq < 1 || total_tokens < 0) return SAGE_ERR_INVALID_ARGUMENT;
+  const sage_status_t s = check_dims(nseq, H, max_seqlen, d);
+  if (s != SAGE_OK) return s;
+  if (total_tokens > (int64_t)nseq * max_seqlen) return SAGE_ERR_INVALID_ARGUMENT;
+  if (total_tokens > 0x7fffffffLL) return SAGE_ERR_INVALID_ARGUMENT;  // cu_seqlens are int32
+  *g = SeqGeom{cu, nseq, H, max_seqlen, d, total_tokens};
+  return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_status_string(sage_status_t s) {
+  switch (s) {
+    case SAGE_OK: return "ok";
+    case SAGE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SAGE_ERR_UNSUPPORTED: return "unsupported";
+    case SAGE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SAGE_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+size_t sage_quant_qk_workspace_size(int B, int H, int d) {
+  if (B < 1 || H < 1 || (d != 64 && d != 128)) return 0;
+  return align_up(sizeof(long long) * (size_t)B * H * d);
+}
+
+sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, sage_layout_t layout,
+                            const int32_t* cu_seqlens, int64_t total_tokens, float sm_scale, int8_t* q_int8,
+                            int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, void* workspace,
+                            size_t workspace_bytes, sage_stream_t stream) {
+  if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
+  SeqGeom g;
+  if (cu_seqlens) {
+    const sage_status_t s = varlen_geom(cu_seqlens, B, N, total_tokens, H, d, &g);
+    if (s != SAGE_OK) return s;
+  } else {
+    const sage_status_t s = check_dims(B, H, N, d);
+    if (s != SAGE_OK) return s;
+    g = SeqGeom{nullptr, B, H, N, d, 0};
+  }
+  if (!q || !k || !q_int8 || !k_int8 || !q_scale || !k_scale || !k_mean || !workspace)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_int8) || !aligned16(k_int8) || !aligned16(q_scale) ||
+      !aligned16(k_scale) || !aligned16(k_mean) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  float sm;
+  if (!resolve_sm_scale(sm_scale, d, &sm)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < sage_quant_qk_workspace_size(g.B, H, d)) return SAGE_ERR_WORKSPACE_TOO_SMALL;
+  if (cu_seqlens && total_tokens == 0) return SAGE_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  sage::launch_quant_qk(g, q, k, sm, q_int8, k_int8, q_scale, k_scale, k_mean,
+                        static_cast<long long*>(workspace), st);
+  return finish(st);
+}
+
+sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_layout_t layout,
+                               const int32_t* cu_seqlens, int64_t total_tokens, uint8_t* v_fp8, float* v_scale,
+                               sage_stream_t stream) {
+  if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
+  SeqGeom g;
+  if (cu_seqlens) {
+    const sage_status_t s = varlen_geom(cu_seqlens, B, N, total_tokens, H, d, &g);
+    if (s != SAGE_OK) return s;
+  } else {
+    const sage_status_t s = check_dims(B, H, N, d);
+    if (s != SAGE_OK) return s;
+    g = SeqGeom{nullptr, B, H, N, d, 0};
+  }
+  if (!v || !v_fp8 || !v_scale) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(v) || !aligned16(v_fp8) || !aligned16(v_scale)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (cu_seqlens && total_tokens == 0) return SAGE_OK;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  sage::launch_v_scale(g, v, v_scale, st);
+  sage::launch_v_prepare(g, v, v_scale, /*fp8=*/true, /*rowmajor=*/true, v_fp8, st);
+  return finish(st);
+}
+
+size_t sage_attn_workspace_size(int B, int H, int N, int d, sage_pv_mode_t pv_mode) {
+  if (check_dims(B, H, N, d) != SAGE_OK) return 0;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
+  return make_layout(false, B, H, N, 0, d, pv_mode == SAGE_PV_FP8_E4M3).total;
+}
+
+sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
+                            sage_layout_t layout, int is_causal, sage_pv_mode_t pv_mode, float sm_scale,
+                            void* workspace, size_t workspace_bytes, sage_stream_t stream) {
+  if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
+  const sage_status_t s = check_dims(B, H, N, d);
+  if (s != SAGE_OK) return s;
+  const SeqGeom g{nullptr, B, H, N, d, 0};
+  return attn_forward(q, k, v, o, g, false, is_causal, pv_mode, sm_scale, workspace, workspace_bytes, stream);
+}
+
+size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H, int d,
+                                       sage_pv_mode_t pv_mode) {
+  if (nseq < 1 || total_tokens < 0 || check_dims(nseq, H, max_seqlen, d) != SAGE_OK) return 0;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
+  return make_layout(true, nseq, H, max_seqlen, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3).total;
+}
+
+sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
+                                   int nseq, int max_seqlen, int64_t total_tokens, int H, int d, int is_causal,
+                                   sage_pv_mode_t pv_mode, float sm_scale, void* workspace, size_t workspace_bytes,
+                                   sage_stream_t stream) {
+  SeqGeom g;
+  const sage_status_t s = varlen_geom(cu_seqlens, nseq, max_seqlen, total_tokens, H, d, &g);
+  if (s != SAGE_OK) return s;
+  return attn_forward(q, k, v, o, g, true, is_causal, pv_mode, sm_scale, workspace, workspace_bytes, stream);
+}
+
+sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int N, int64_t total_tokens, int d,
+                                         sage_pv_mode_t pv_mode, size_t offsets_out[8]) {
+  if (!offsets_out) return SAGE_ERR_INVALID_ARGUMENT;
+  if (check_dims(B, H, N, d) != SAGE_OK) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (varlen && total_tokens < 0) return SAGE_ERR_INVALID_ARGUMENT;
+  const WsLayout L = make_layout(varlen != 0, B, H, N, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3);
+  for (int i = 0; i < 7; ++i) offsets_out[i] = L.off[i];
+  offsets_out[7] = L.total;
+  return SAGE_OK;
+}
+
+sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int N, int d, int is_causal,
+                                            sage_pv_mode_t pv_mode, const void* workspace, size_t workspace_bytes,
+                                            sage_stream_t stream) {
+  const sage_status_t s = check_dims(B, H, N, d);
+  if (s != SAGE_OK) return s;
+  if (!o || !workspace || !aligned16(o) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
+  const WsLayout L = make_layout(false, B, H, N, 0, d, fp8);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
+  const size_t tensor_bytes = (size_t)B * H * N * d * 2;
+  if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
+  const char* ws = static_cast<const char*>(workspace);
+  const SeqGeom g{nullptr, B, H, N, d, 0};
+  sage::AttnArgs a{reinterpret_cast<const int8_t*>(ws + L.off[0]), reinterpret_cast<const int8_t*>(ws + L.off[1]),
+                   reinterpret_cast<const float*>(ws + L.off[2]), reinterpret_cast<const float*>(ws + L.off[3]),
+                   reinterpret_cast<const uint8_t*>(ws + L.off[5]), reinterpret_cast<const float*>(ws + L.off[6]),
+                   static_cast<uint16_t*>(o), g};
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  sage::launch_attn(a, is_causal != 0, fp8, st);
+  return finish(st);
+}
+
+sage_status_t sage_test_qk_tiles(const int8_t* q_int8, const int8_t* k_int8, int B, int H, int N, int d,
+                                 const int32_t* tile_list, int n_tiles, int32_t* out, sage_stream_t stream) {
+  const sage_status_t s = check_dims(B, H, N, d);
+  if (s != SAGE_OK) return s;
+  if (!q_int8 || !k_int8 || !tile_list || !out || n_tiles < 1) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q_int8) || !aligned16(k_int8) || !aligned16(tile_list) || !aligned16(out))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  sage::launch_qk_tiles(q_int8, k_int8, B, H, N, d, tile_list, n_tiles, out, st);
+  return finish(st);
+}
+
+}  // extern "C"

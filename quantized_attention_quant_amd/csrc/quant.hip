@@ -1,0 +1,381 @@
+// Pre-pass kernels: K smoothing, per-block INT8 quantisation of Q and K, and
+// V preparation (packed FP16 tiles, or per-channel e4m3) for the attention
+// kernel.  All of them are HBM-bound streaming kernels: 16-byte coalesced
+// loads, one workgroup per quantisation block, values kept in registers
+// between the block reduction and the quantisation (one read of each input).
+//
+// Pages (by title): "⚡️SageAttention — brand new attention" (postsniper.ru),
+// quantisation introduction: scale = max|A|/127, Â = round(A/scale); dtcms.com
+// SageAttention summary, section "SageAttention（v1）": smooth K by its mean,
+// per-block quantisation of q and k; section "SageAttention 2": V in FP8.
+#include "sage_common.h"
+#include "sage_internal.h"
+
+namespace sage {
+
+// ---------------------------------------------------------------------------
+// Zero fill (used instead of hipMemsetAsync so the sequence stays capturable).
+__global__ void zero_kernel(v4i* __restrict__ p, int64_t n16) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n16) p[i] = v4i{0, 0, 0, 0};
+}
+
+// ---------------------------------------------------------------------------
+// K column sums in exact int64 fixed point (value * 2^24), per head-sequence.
+// Grid (ceil(Nmax/256), H, B); each block sums up to 256 tokens and adds its
+// partial sums with integer atomics (exact and order-independent).
+constexpr int kColsumChunk = 256;
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_colsum_kernel(const uint16_t* __restrict__ k, SeqGeom g,
+                                                            unsigned long long* __restrict__ colsum) {
+  constexpr int CG = D / 8;            // 16-byte channel groups per row
+  constexpr int RPP = kThreads / CG;   // rows per pass
+  const int b = blockIdx.z, h = blockIdx.y;
+  int64_t row0;
+  int n;
+  hs_rows(g, b, h, row0, n);
+  const int t0 = blockIdx.x * kColsumChunk;
+  if (t0 >= n) return;
+  const int t1 = min(n, t0 + kColsumChunk);
+  const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
+  int64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t = t0 + rr; t < t1; t += RPP) {
+    const v4i raw = *reinterpret_cast<const v4i*>(k + (row0 + t) * D + cg * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = (uint32_t)raw[j];
+      acc[2 * j] += fp16_fixed24((uint16_t)(w & 0xffffu));
+      acc[2 * j + 1] += fp16_fixed24((uint16_t)(w >> 16));
+    }
+  }
+  __shared__ int64_t red[RPP][D];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rr][cg * 8 + j] = acc[j];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    int64_t s = 0;
+    for (int r = 0; r < RPP; ++r) s += red[r][threadIdx.x];
+    const int64_t hs = (int64_t)b * g.H + h;
+    atomicAdd(colsum + hs * D + threadIdx.x, (unsigned long long)s);
+  }
+}
+
+// Block-wide max of a non-negative value over 256 threads.
+__device__ __forceinline__ float block_max256(float v) {
+  __shared__ float wmax[kThreads / 64];
+  v = wave_max(v);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float r = wmax[0];
+#pragma unroll
+  for (int i = 1; i < kThreads / 64; ++i) r = fmaxf(r, wmax[i]);
+  return r;
+}
+
+// Symmetric INT8 code of x with block scale s (s == 0 -> 0): IEEE fp32 divide,
+// round half to even, clamp to ±127.
+__device__ __forceinline__ int int8_code(float x, float s) {
+  if (!(s > 0.f)) return 0;
+  const float r = __builtin_rintf(x / s);
+  return (int)fminf(fmaxf(r, -kInt8Max), kInt8Max);
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
+// ---------------------------------------------------------------------------
+// Per-block INT8 of one block of ROWS tokens x D channels of fp32 values
+// x = fp16 input - shift; SMOOTH selects the K path (shift = token mean).
+// Grid (ceil(Nmax/ROWS), H, B).
+template <int D, int ROWS, bool SMOOTH>
+__global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* __restrict__ x16, SeqGeom g,
+                                                               const long long* __restrict__ colsum,
+                                                               float out_scale_mul, int8_t* __restrict__ codes,
+                                                               float* __restrict__ scales,
+                                                               float* __restrict__ kmean) {
+  constexpr int CG = D / 8, RPP = kThreads / CG, PASSES = ROWS / RPP;
+  static_assert(PASSES * RPP == ROWS, "block rows must be a multiple of rows per pass");
+  const int b = blockIdx.z, h = blockIdx.y, blk = blockIdx.x;
+  int64_t row0;
+  int n;
+  hs_rows(g, b, h, row0, n);
+  const int t0 = blk * ROWS;
+  if (t0 >= n) return;
+  const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
+  const int64_t hs = (int64_t)b * g.H + h;
+  float shift[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) shift[j] = 0.f;
+  if (SMOOTH) {
+    // km = fp32(exact sum * 2^-24 / n): one fp64 divide, one rounding.
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      shift[j] = (float)((double)colsum[hs * D + cg * 8 + j] * 0x1p-24 / (double)n);
+    if (blk == 0 && rr == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kmean[hs * D + cg * 8 + j] = shift[j];
+    }
+  }
+  float x[PASSES][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + rr + p * RPP;
+    if (t < n) {
+      const v4i raw = *reinterpret_cast<const v4i*>(x16 + (row0 + t) * D + cg * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = (uint32_t)raw[j];
+        const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+        const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+        x[p][2 * j] = lo - shift[2 * j];
+        x[p][2 * j + 1] = hi - shift[2 * j + 1];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[p][j] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[p][j]));
+  }
+  amax = block_max256(amax);
+  const float s = amax / kInt8Max;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + rr + p * RPP;
+    if (t < n) {
+      uint2 w;
+      w.x = pack4_i8(int8_code(x[p][0], s), int8_code(x[p][1], s), int8_code(x[p][2], s), int8_code(x[p][3], s));
+      w.y = pack4_i8(int8_code(x[p][4], s), int8_code(x[p][5], s), int8_code(x[p][6], s), int8_code(x[p][7], s));
+      *reinterpret_cast<uint2*>(codes + (row0 + t) * D + cg * 8) = w;
+    }
+  }
+  if (threadIdx.x == 0) {
+    const int nblk = ceil_div(g.N, ROWS);
+    scales[hs * nblk + blk] = s * out_scale_mul;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// V per-channel absolute maximum (as fp32 bits; non-negative floats order like
+// their bit patterns, so an integer atomic max is exact).
+template <int D>
+__global__ __launch_bounds__(kThreads) void v_absmax_kernel(const uint16_t* __restrict__ v, SeqGeom g,
+                                                            unsigned* __restrict__ amax_bits) {
+  constexpr int CG = D / 8, RPP = kThreads / CG;
+  const int b = blockIdx.z, h = blockIdx.y;
+  int64_t row0;
+  int n;
+  hs_rows(g, b, h, row0, n);
+  const int t0 = blockIdx.x * kColsumChunk;
+  if (t0 >= n) return;
+  const int t1 = min(n, t0 + kColsumChunk);
+  const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
+  float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int t = t0 + rr; t < t1; t += RPP) {
+    const v4i raw = *reinterpret_cast<const v4i*>(v + (row0 + t) * D + cg * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = (uint32_t)raw[j];
+      m[2 * j] = fmaxf(m[2 * j], fabsf((float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu))));
+      m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf((float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16))));
+    }
+  }
+  __shared__ float red[RPP][D];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rr][cg * 8 + j] = m[j];
+  __syncthreads();
+  if (threadIdx.x < D) {
+    float s = 0.f;
+    for (int r = 0; r < RPP; ++r) s = fmaxf(s, red[r][threadIdx.x]);
+    const int64_t hs = (int64_t)b * g.H + h;
+    atomicMax(amax_bits + hs * D + threadIdx.x, __float_as_uint(s));
+  }
+}
+
+// scale = fp32(amax / 448), in place over the amax bits.
+__global__ void v_scale_finalize_kernel(float* __restrict__ vs, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) vs[i] = vs[i] / kE4M3Max;
+}
+
+// OCP e4m3 byte of fp32(v / s): IEEE divide, saturate to ±448, then the
+// hardware round-to-nearest-even conversion.  s == 0 -> code 0.
+__device__ __forceinline__ float e4m3_operand(float v, float s) {
+  if (!(s > 0.f)) return 0.f;
+  return __builtin_amdgcn_fmed3f(v / s, -kE4M3Max, kE4M3Max);
+}
+
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// ---------------------------------------------------------------------------
+// V preparation, one 64-key tile per workgroup.  Grid (ceil(Nmax/64), H, B).
+//   FP8 = false: packed fp16 tile in MFMA-operand order (see attn.hip).
+//   FP8 = true, ROWMAJOR = false: packed e4m3 tile in MFMA-operand order.
+//   FP8 = true, ROWMAJOR = true: row-major e4m3 codes [.., n, D].
+// Packed fp16 tile: 16-byte chunk (f, lane), f = kc*(D/32) + dt, holds the
+//   8 values V[key][d] with d = 32dt + lane%32 and, for j = 0..7,
+//   key = 16kc + 8(j/4) + 4(lane/32) + j%4.
+// Packed e4m3 tile: 32-byte chunk (dt, lane) holds, for j = 0..31,
+//   key = 32(j/16) + 8((j%16)/4) + 4(lane/32) + j%4, d = 32dt + lane%32.
+// Keys past the sequence end are written as zeros.
+template <int D, bool FP8, bool ROWMAJOR>
+__global__ __launch_bounds__(kThreads) void v_prepare_kernel(const uint16_t* __restrict__ v, SeqGeom g,
+                                                             const float* __restrict__ vscale,
+                                                             uint8_t* __restrict__ out) {
+  const int b = blockIdx.z, h = blockIdx.y, kb = blockIdx.x;
+  int64_t row0;
+  int n;
+  hs_rows(g, b, h, row0, n);
+  const int t0 = kb * kKBlock;
+  if (t0 >= n) return;
+  const int64_t hs = (int64_t)b * g.H + h;
+  __shared__ uint16_t tile[kKBlock][D + 2];
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  for (int idx = threadIdx.x; idx < kKBlock * CPR; idx += kThreads) {
+    const int r = idx / CPR, c = idx % CPR;
+    v4i val = {0, 0, 0, 0};
+    if (t0 + r < n) val = *reinterpret_cast<const v4i*>(v + (row0 + t0 + r) * D + c * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[r][c * 8 + 2 * j] = (uint16_t)((uint32_t)val[j] & 0xffffu);
+      tile[r][c * 8 + 2 * j + 1] = (uint16_t)((uint32_t)val[j] >> 16);
+    }
+  }
+  __syncthreads();
+  if (!FP8) {
+    constexpr int TILE_BYTES = kKBlock * D * 2;
+    uint8_t* dst = out + vtile_index(g, b, h, kb) * TILE_BYTES;
+    for (int idx = threadIdx.x; idx < TILE_BYTES / 16; idx += kThreads) {
+      const int f = idx / 64, lane = idx % 64;
+      const int kc = f / (D / 32), dt = f % (D / 32);
+      const int d = 32 * dt + (lane & 31), g4 = 4 * (lane >> 5);
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const int k0 = 16 * kc + 8 * (j / 4) + g4 + (j & 3);
+        w[j / 2] = (uint32_t)tile[k0][d] | ((uint32_t)tile[k0 + 1][d] << 16);
+      }
+      *reinterpret_cast<v4i*>(dst + (int64_t)idx * 16) = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+  } else if (!ROWMAJOR) {
+    constexpr int TILE_BYTES = kKBlock * D;
+    uint8_t* dst = out + vtile_index(g, b, h, kb) * TILE_BYTES;
+    for (int idx = threadIdx.x; idx < TILE_BYTES / 32; idx += kThreads) {
+      const int dt = idx / 64, lane = idx % 64;
+      const int d = 32 * dt + (lane & 31), g4 = 4 * (lane >> 5);
+      const float s = vscale[hs * D + d];
+      uint32_t w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        float f[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int j = 4 * q + jj;
+          const int key = 32 * (j / 16) + 8 * ((j % 16) / 4) + g4 + (j & 3);
+          f[jj] = e4m3_operand((float)__builtin_bit_cast(_Float16, tile[key][d]), s);
+        }
+        w[q] = pack4_e4m3(f[0], f[1], f[2], f[3]);
+      }
+      v4i* o = reinterpret_cast<v4i*>(dst + (int64_t)idx * 32);
+      o[0] = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+      o[1] = v4i{(int)w[4], (int)w[5], (int)w[6], (int)w[7]};
+    }
+  } else {
+    // row-major codes: each thread converts 16 channels of one row
+    constexpr int C16 = D / 16;
+    for (int idx = threadIdx.x; idx < kKBlock * C16; idx += kThreads) {
+      const int r = idx / C16, c = idx % C16;
+      if (t0 + r >= n) continue;
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float f[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d = 16 * c + 4 * q + jj;
+          f[jj] = e4m3_operand((float)__builtin_bit_cast(_Float16, tile[r][d]), vscale[hs * D + d]);
+        }
+        w[q] = pack4_e4m3(f[0], f[1], f[2], f[3]);
+      }
+      *reinterpret_cast<v4i*>(out + (row0 + t0 + r) * D + 16 * c) =
+          v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launchers.
+static inline dim3 hs_grid(const SeqGeom& g, int rows) { return dim3(ceil_div(g.N, rows), g.H, g.B); }
+
+void launch_zero(void* p, size_t bytes, hipStream_t st) {
+  const int64_t n16 = (int64_t)(bytes / 16);
+  if (n16 == 0) return;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)ceil_div64(n16, 256)), dim3(256), 0, st,
+                     reinterpret_cast<v4i*>(p), n16);
+}
+
+void launch_quant_qk(const SeqGeom& g, const void* q, const void* k, float sm_scale, int8_t* q_int8,
+                     int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, long long* colsum,
+                     hipStream_t st) {
+  const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+  const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
+  launch_zero(colsum, sizeof(long long) * (size_t)g.B * g.H * g.d, st);
+  if (g.d == 128) {
+    hipLaunchKernelGGL((k_colsum_kernel<128>), hs_grid(g, kColsumChunk), dim3(kThreads), 0, st, k16, g,
+                       reinterpret_cast<unsigned long long*>(colsum));
+    hipLaunchKernelGGL((quant_block_kernel<128, kQBlock, false>), hs_grid(g, kQBlock), dim3(kThreads), 0, st,
+                       q16, g, (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);
+    hipLaunchKernelGGL((quant_block_kernel<128, kKBlock, true>), hs_grid(g, kKBlock), dim3(kThreads), 0, st,
+                       k16, g, (const long long*)colsum, 1.0f, k_int8, k_scale, k_mean);
+  } else {
+    hipLaunchKernelGGL((k_colsum_kernel<64>), hs_grid(g, kColsumChunk), dim3(kThreads), 0, st, k16, g,
+                       reinterpret_cast<unsigned long long*>(colsum));
+    hipLaunchKernelGGL((quant_block_kernel<64, kQBlock, false>), hs_grid(g, kQBlock), dim3(kThreads), 0, st,
+                       q16, g, (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);
+    hipLaunchKernelGGL((quant_block_kernel<64, kKBlock, true>), hs_grid(g, kKBlock), dim3(kThreads), 0, st,
+                       k16, g, (const long long*)colsum, 1.0f, k_int8, k_scale, k_mean);
+  }
+}
+
+void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st) {
+  const uint16_t* v16 = reinterpret_cast<const uint16_t*>(v);
+  const int64_t count = (int64_t)g.B * g.H * g.d;
+  launch_zero(v_scale, sizeof(float) * (size_t)count, st);  // count is a multiple of 64
+  if (g.d == 128)
+    hipLaunchKernelGGL((v_absmax_kernel<128>), hs_grid(g, kColsumChunk), dim3(kThreads), 0, st, v16, g,
+                       reinterpret_cast<unsigned*>(v_scale));
+  else
+    hipLaunchKernelGGL((v_absmax_kernel<64>), hs_grid(g, kColsumChunk), dim3(kThreads), 0, st, v16, g,
+                       reinterpret_cast<unsigned*>(v_scale));
+  hipLaunchKernelGGL(v_scale_finalize_kernel, dim3((unsigned)ceil_div64(count, 256)), dim3(256), 0, st, v_scale,
+                     count);
+}
+
+void launch_v_prepare(const SeqGeom& g, const void* v, const float* v_scale, bool fp8, bool rowmajor,
+                      void* out, hipStream_t st) {
+  const uint16_t* v16 = reinterpret_cast<const uint16_t*>(v);
+  uint8_t* o = reinterpret_cast<uint8_t*>(out);
+  const dim3 grid = hs_grid(g, kKBlock);
+#define SAGE_VPREP(DD, F8, RM) \
+  hipLaunchKernelGGL((v_prepare_kernel<DD, F8, RM>), grid, dim3(kThreads), 0, st, v16, g, v_scale, o)
+  if (g.d == 128) {
+    if (!fp8) SAGE_VPREP(128, false, false);
+    else if (!rowmajor) SAGE_VPREP(128, true, false);
+    else SAGE_VPREP(128, true, true);
+  } else {
+    if (!fp8) SAGE_VPREP(64, false, false);
+    else if (!rowmajor) SAGE_VPREP(64, true, false);
+    else SAGE_VPREP(64, true, true);
+  }
+#undef SAGE_VPREP
+}
+
+}  // namespace sage

@@ -1,0 +1,91 @@
+// Device-side definitions shared by the pre-pass and attention kernels.
+// gfx950 (CDNA4) only: 64-lane wavefronts, MFMA matrix cores, 160 KB LDS/CU.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+// Geometry of the method (dtcms SageAttention summary, "SageAttention（v1）":
+// per-block quantisation; block sizes are this implementation's reading).
+constexpr int kQBlock = 128;  // tokens per Q scale block == queries per workgroup
+constexpr int kKBlock = 64;   // tokens per K scale block == keys per attention tile
+constexpr int kThreads = 256; // 4 wavefronts of 64
+constexpr float kInt8Max = 127.0f;
+constexpr float kE4M3Max = 448.0f;
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// One "head-sequence": a (batch entry, head) of a dense [B,H,N,d] tensor or a
+// (sequence, head) of a packed [H,T,d] tensor.  Everything the method does per
+// block, mean or mask stays inside one head-sequence.
+struct SeqGeom {
+  const int32_t* cu;  // varlen offsets (device) or nullptr for dense
+  int B;              // batch size (dense) or number of sequences (varlen)
+  int H;
+  int N;              // tokens per sequence (dense) or maximum length (varlen)
+  int d;
+  int64_t T;          // total packed tokens (varlen)
+};
+
+// First token row (in units of d elements) and length of head-sequence (b, h).
+__device__ __forceinline__ void hs_rows(const SeqGeom& g, int b, int h, int64_t& row0, int& n) {
+  if (g.cu) {
+    const int s = g.cu[b], e = g.cu[b + 1];
+    n = e - s;
+    row0 = (int64_t)h * g.T + s;
+  } else {
+    n = g.N;
+    row0 = ((int64_t)b * g.H + h) * g.N;
+  }
+}
+
+__host__ __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ __forceinline__ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Packed-V tiles: one tile = 64 keys x d channels, laid out in the order the
+// attention kernel's MFMA lanes consume it.  Dense: tiles of head-sequence
+// (b,h) are contiguous.  Varlen: head-major; sequence i of head h starts at
+// tile floor(cu[i]/64) + i, which never overlaps its neighbours and needs only
+// cu[i] to compute.
+__host__ __device__ __forceinline__ int64_t vtiles_per_head_varlen(int64_t T, int nseq) {
+  return ceil_div64(T, kKBlock) + nseq;
+}
+__device__ __forceinline__ int64_t vtile_index(const SeqGeom& g, int b, int h, int kb) {
+  if (g.cu) {
+    return (int64_t)h * vtiles_per_head_varlen(g.T, g.B) + g.cu[b] / kKBlock + b + kb;
+  }
+  return ((int64_t)b * g.H + h) * ceil_div(g.N, kKBlock) + kb;
+}
+
+// Map a workgroup id onto a logical work index so that consecutive logical
+// indices run on the same XCD.  Workgroups are dispatched round-robin over the
+// 8 XCDs; XCD x receives ids x, x+8, ...; it is given the contiguous logical
+// range [x*q + min(x, r), ...) where total = 8q + r.  A bijection on [0,total).
+__device__ __forceinline__ int xcd_remap(int bid, int total) {
+  constexpr int kXcd = 8;
+  const int q = total / kXcd, r = total % kXcd;
+  const int x = bid % kXcd, local = bid / kXcd;
+  return x * q + (x < r ? x : r) + local;
+}
+
+// fp16 bits -> exact integer value * 2^24 (every fp16 is a multiple of 2^-24).
+__device__ __forceinline__ int64_t fp16_fixed24(uint16_t hbits) {
+  const int e = (hbits >> 10) & 31;
+  const int m = hbits & 1023;
+  const int64_t mag = e == 0 ? (int64_t)m : ((int64_t)(1024 + m) << (e - 1));
+  return (hbits & 0x8000) ? -mag : mag;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace sage

@@ -1,0 +1,31 @@
+// Host-side launchers shared between the C ABI and the kernel translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include "sage_common.h"
+
+namespace sage {
+
+struct AttnArgs {
+  const int8_t* q;         // Q codes, same layout as the fp16 input
+  const int8_t* k;         // K codes
+  const float* q_scale;    // [B][H][nqb], softmax scale folded in
+  const float* k_scale;    // [B][H][nkb]
+  const uint8_t* v_packed; // packed V tiles (fp16 or e4m3)
+  const float* v_scale;    // [B][H][d] (FP8 mode)
+  uint16_t* o;             // fp16 output, same layout as the input
+  SeqGeom g;
+};
+
+void launch_zero(void* p, size_t bytes, hipStream_t st);
+void launch_quant_qk(const SeqGeom& g, const void* q, const void* k, float sm_scale, int8_t* q_int8,
+                     int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, long long* colsum,
+                     hipStream_t st);
+void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st);
+void launch_v_prepare(const SeqGeom& g, const void* v, const float* v_scale, bool fp8, bool rowmajor,
+                      void* out, hipStream_t st);
+void launch_attn(const AttnArgs& a, bool causal, bool fp8, hipStream_t st);
+void launch_qk_tiles(const int8_t* q, const int8_t* k, int B, int H, int N, int d, const int32_t* list,
+                     int n, int32_t* out, hipStream_t st);
+
+}  // namespace sage

@@ -1,0 +1,132 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before touching the device.
+No call here reaches a kernel launch (CPU only)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import quantized_attention_quant_amd as sage
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage.h")
+
+INVALID, UNSUPPORTED, WS_SMALL = 1, 2, 3
+ALIGNED = 0x10000      # a fake, 256-byte aligned device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_built_and_loads():
+    assert os.path.exists(sage.LIB_PATH), "run __graft_entry__.build() first"
+    sage.lib()
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", sage.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sage_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(sage.SIGNATURES) == set(names)
+
+
+def test_status_strings():
+    assert sage.sage_status_string(0) == "ok"
+    assert sage.sage_status_string(3) == "workspace too small"
+    assert sage.sage_status_string(99) == "unknown status"
+
+
+def test_workspace_sizes():
+    assert sage.sage_quant_qk_workspace_size(2, 3, 64) >= 2 * 3 * 64 * 8
+    assert sage.sage_quant_qk_workspace_size(2, 3, 96) == 0
+    w16 = sage.sage_attn_workspace_size(1, 2, 256, 64, "fp16")
+    w8 = sage.sage_attn_workspace_size(1, 2, 256, 64, "fp8")
+    # two int8 copies + packed V (fp16 twice the size of e4m3) dominate
+    assert w16 >= 2 * 1 * 2 * 256 * 64 + 2 * 256 * 64 * 2
+    assert w8 < w16
+    assert sage.sage_attn_workspace_size(1, 2, 0, 64, "fp16") == 0
+    wv = sage.sage_attn_varlen_workspace_size(3, 200, 271, 2, 128, "fp16")
+    assert wv >= 2 * 2 * 271 * 128
+    offs = sage.sage_test_workspace_layout(False, 1, 2, 256, 0, 64, "fp8")
+    assert offs[7] == w8
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs)
+
+
+def _fwd(**over):
+    a = dict(q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, o=ALIGNED * 4, B=1, H=2, N=256, d=64, layout=0,
+             causal=0, pv=0, sm=0.0, ws=ALIGNED * 8, wsb=1 << 30, stream=None)
+    a.update(over)
+    return sage.lib().sage_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["d"], a["layout"],
+                                    a["causal"], a["pv"], a["sm"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(q=ALIGNED + 8), INVALID),          # not 16-byte aligned
+    (dict(ws=ALIGNED * 8 + 16), INVALID),    # workspace not 256-byte aligned
+    (dict(d=96), INVALID),
+    (dict(d=0), INVALID),
+    (dict(N=0), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(H=0), INVALID),
+    (dict(N=(1 << 23) + 1), INVALID),
+    (dict(pv=2), INVALID),
+    (dict(layout=1), UNSUPPORTED),
+    (dict(sm=float("nan")), INVALID),
+    (dict(sm=float("inf")), INVALID),
+    (dict(wsb=100), WS_SMALL),
+    (dict(o=ALIGNED), INVALID),              # output aliases q
+])
+def test_attn_fwd_rejects(over, status):
+    assert _fwd(**over) == status
+
+
+def test_varlen_rejects():
+    L = sage.lib()
+    f = L.sage_attn_varlen_fwd
+    args = [ALIGNED, ALIGNED * 2, ALIGNED * 3, ALIGNED * 4, ALIGNED * 5, 3, 128, 300, 2, 64, 1, 0, 0.0,
+            ALIGNED * 8, 1 << 30, None]
+    bad = list(args); bad[4] = None                 # cu_seqlens
+    assert f(*bad) == INVALID
+    bad = list(args); bad[5] = 0                    # nseq
+    assert f(*bad) == INVALID
+    bad = list(args); bad[7] = 3 * 128 + 1          # more tokens than nseq * max_seqlen
+    assert f(*bad) == INVALID
+    bad = list(args); bad[7] = -1
+    assert f(*bad) == INVALID
+    bad = list(args); bad[14] = 10
+    assert f(*bad) == WS_SMALL
+
+
+def test_quant_rejects():
+    L = sage.lib()
+    st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, None, ALIGNED * 3, ALIGNED * 4,
+                         ALIGNED * 5, ALIGNED * 6, ALIGNED * 8, 1 << 20, None)
+    assert st == INVALID
+    st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, ALIGNED * 9, ALIGNED * 3,
+                         ALIGNED * 4, ALIGNED * 5, ALIGNED * 6, ALIGNED * 8, 8, None)
+    assert st == WS_SMALL
+    st = L.sage_quant_v_fp8(ALIGNED, 1, 2, 256, 100, 0, None, 0, ALIGNED * 2, ALIGNED * 3, None)
+    assert st == INVALID
+    st = L.sage_test_qk_tiles(ALIGNED, ALIGNED * 2, 1, 1, 128, 64, ALIGNED * 3, 0, ALIGNED * 4, None)
+    assert st == INVALID
+    arr = (ctypes.c_size_t * 8)()
+    assert L.sage_test_workspace_layout(0, 1, 1, 128, 0, 80, 0, arr) == INVALID
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(sage, "_lib", None)
+    monkeypatch.setattr(sage, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(sage.SageError):
+        sage.lib()

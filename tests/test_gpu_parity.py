@@ -1,0 +1,310 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars
+  * INT8 Q̂/K̂, their block scales, the K means, e4m3 V̂ and its per-channel
+    scales, and the int32 Q̂K̂ᵀ tiles: bit-exact.
+  * fp16 output vs the method (oracle O1): max-abs <= 2e-2 and cosine >=
+    0.9995; vs fp64 exact attention (O2): cosine >= 0.998 (the pages' per-layer
+    bar), except the video-DiT literal reading, held to min(0.998, cos_O1 - 1e-4).
+Small shapes compare every row; the full-size workloads compare sampled rows
+of sampled heads, in the same launch configuration the benchmark times.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_attention_quant_amd as sage
+import workloads
+from oracle import sage_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+COS_O1 = 0.9995
+COS_O2 = 0.998
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def cos(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / (np.linalg.norm(a) * np.linalg.norm(b)))
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(name):
+    return workloads.generate(workloads.get(name))
+
+
+def check_out(ours, o1, o2, label, o2_floor=COS_O2):
+    ours = np.asarray(ours, np.float64)
+    assert np.isfinite(ours).all(), label
+    err = np.abs(ours - o1.astype(np.float64)).max()
+    c1 = cos(ours, o1)
+    c2 = cos(ours, o2)
+    say(f"{label}: max_abs_vs_O1={err:.3e} cos_O1={c1:.6f} cos_O2={c2:.6f}")
+    assert err <= MAX_ABS, (label, err)
+    assert c1 >= COS_O1, (label, c1)
+    assert c2 >= o2_floor, (label, c2)
+
+
+# ---------------------------------------------------------------------------
+# Small shapes: every row, ragged tails, both head dims, both PV modes
+# ---------------------------------------------------------------------------
+SMALL = [(n, d) for d in (64, 128) for n in (1, 63, 64, 65, 127, 129, 200, 257)]
+
+
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d", SMALL)
+def test_small_all_rows(n, d, causal, pv_mode):
+    say(f"case small n={n} d={d} causal={causal} pv={pv_mode}")
+    x = workloads.generate_custom(100 + n + d, 2, 3, n, d, k_bias=3.0, q_bias=1.0)
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    o = host(sage.sage_attn_fwd(q, k, v, is_causal=causal, pv_mode=pv_mode))
+    quant = O.quant_qk_dense(x.q, x.k)
+    vc, vs = O.quant_v_fp8(x.v)
+    rows = np.arange(n)
+    for b in range(2):
+        for h in range(3):
+            qi, qs, ki, ks = O.head_views_dense(quant, b, h)
+            if pv_mode == "fp8":
+                o1 = O.sage_attention_rows(qi, qs, ki, ks, vc[b, h], rows, causal, "fp8", vs[b, h])
+            else:
+                o1 = O.sage_attention_rows(qi, qs, ki, ks, x.v[b, h], rows, causal, "fp16")
+            o2 = O.sdpa_fp64_rows(x.q[b, h], x.k[b, h], x.v[b, h], rows, causal)
+            check_out(o[b, h], o1, o2, f"n={n} d={d} b={b} h={h}")
+            if n == 1 or causal:
+                # one visible key: the output is V itself (fp16 PV, bit-exact) or its e4m3
+                # dequantisation (fp8 PV; within one fp16 ulp, since the kernel's row sum is
+                # 448*2^e with |e| ~ 1e-6 from fp32 rounding of the running max)
+                if pv_mode == "fp16":
+                    assert (o[b, h, 0].view(np.uint16) == x.v[b, h, 0].view(np.uint16)).all()
+                else:
+                    want = (O.e4m3_decode(vc[b, h, 0]) * vs[b, h].astype(np.float64)).astype(np.float16)
+                    ulp = np.spacing(np.abs(want)).astype(np.float64)
+                    assert (np.abs(o[b, h, 0].astype(np.float64) - want) <= ulp).all()
+
+
+@pytest.mark.parametrize("n,d", [(1, 64), (65, 128), (300, 64), (1000, 128)])
+def test_quant_qk_bit_exact_small(n, d):
+    say(f"case quant small n={n} d={d}")
+    x = workloads.generate_custom(7 + n, 2, 2, n, d, k_bias=3.0)
+    got = {k2: host(v2) for k2, v2 in sage.sage_quant_qk(dev(x.q), dev(x.k)).items()}
+    ref = O.quant_qk_dense(x.q, x.k)
+    for key in ("q_int8", "k_int8", "q_scale", "k_scale", "k_mean"):
+        assert got[key].shape == ref[key].shape, key
+        assert (got[key].view(np.uint8) == ref[key].view(np.uint8)).all(), key
+    # custom softmax scale is folded the same way
+    got2 = host(sage.sage_quant_qk(dev(x.q), dev(x.k), sm_scale=0.3)["q_scale"])
+    ref2 = O.quant_qk_dense(x.q, x.k, sm_scale=0.3)["q_scale"]
+    assert (got2.view(np.uint32) == ref2.view(np.uint32)).all()
+
+
+def test_quant_zero_blocks_and_constant_k():
+    say("case quant zero blocks")
+    q = np.zeros((1, 1, 300, 64), np.float16)
+    q[0, 0, 128:256] = 2.0
+    k = np.full((1, 1, 300, 64), 1.5, np.float16)   # smoothing makes K exactly zero
+    got = {k2: host(v2) for k2, v2 in sage.sage_quant_qk(dev(q), dev(k)).items()}
+    ref = O.quant_qk_dense(q, k)
+    for key in ref:
+        assert (got[key].view(np.uint8) == ref[key].view(np.uint8)).all(), key
+    assert (got["k_scale"] == 0).all() and (got["k_int8"] == 0).all()
+    v = np.random.default_rng(1).standard_normal((1, 1, 300, 64)).astype(np.float16)
+    o = host(sage.sage_attn_fwd(dev(q), dev(k), dev(v)))
+    assert np.isfinite(o.astype(np.float64)).all()
+    want = v[0, 0].astype(np.float64).mean(axis=0)
+    assert np.abs(o[0, 0].astype(np.float64) - want).max() < 2e-3
+
+
+def test_quant_v_fp8_bit_exact_small():
+    say("case quant v fp8 small")
+    rng = np.random.default_rng(3)
+    v = (rng.standard_normal((2, 3, 131, 128)) * rng.choice([0.01, 1, 40], size=(1, 3, 1, 128))).astype(np.float16)
+    v[0, 1, :, 5] = 0
+    codes, scale = sage.sage_quant_v_fp8(dev(v))
+    rc, rs = O.quant_v_fp8(v)
+    assert (host(scale).view(np.uint32) == rs.view(np.uint32)).all()
+    assert (host(codes) == rc).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_qk_tiles_bit_exact(d):
+    say(f"case qk tiles d={d}")
+    x = workloads.generate_custom(55 + d, 2, 2, 300, d, k_bias=3.0)
+    quant = sage.sage_quant_qk(dev(x.q), dev(x.k))
+    qi, ki = host(quant["q_int8"]), host(quant["k_int8"])
+    tiles = np.array([(b, h, qb, kb) for b in range(2) for h in range(2) for qb in range(3) for kb in range(5)]
+                     + [(0, 0, 5, 0), (0, 9, 0, 0)], np.int32)
+    got = host(sage.sage_test_qk_tiles(quant["q_int8"], quant["k_int8"], dev(tiles)))
+    for t, (b, h, qb, kb) in enumerate(tiles.tolist()):
+        want = np.zeros((128, 64), np.int64)
+        if h < 2 and qb < 3:
+            qa = np.zeros((128, d), np.int8)
+            ka = np.zeros((64, d), np.int8)
+            qs = qi[b, h, qb * 128:(qb + 1) * 128]
+            ks = ki[b, h, kb * 64:(kb + 1) * 64]
+            qa[:len(qs)] = qs
+            ka[:len(ks)] = ks
+            want = O.qk_int(qa, ka)
+        assert (got[t] == want).all(), (b, h, qb, kb)
+
+
+def test_deterministic_and_workspace_matches_quant():
+    say("case determinism")
+    x = workloads.generate_custom(77, 1, 4, 1000, 128, k_bias=3.0)
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    for pv_mode in ("fp16", "fp8"):
+        size = sage.sage_attn_workspace_size(1, 4, 1000, 128, pv_mode)
+        ws = torch.empty(size, dtype=torch.uint8, device="cuda")
+        outs = [host(sage.sage_attn_fwd(q, k, v, is_causal=True, pv_mode=pv_mode, workspace=ws)) for _ in range(3)]
+        for o in outs[1:]:
+            assert (o.view(np.uint16) == outs[0].view(np.uint16)).all()
+        offs = sage.sage_test_workspace_layout(False, 1, 4, 1000, 0, 128, pv_mode)
+        ref = sage.sage_quant_qk(q, k)
+        wsn = host(ws)
+        n8 = 4 * 1000 * 128
+        assert (wsn[offs[0]:offs[0] + n8].view(np.int8) == host(ref["q_int8"]).ravel()).all()
+        assert (wsn[offs[1]:offs[1] + n8].view(np.int8) == host(ref["k_int8"]).ravel()).all()
+        nq, nk = 4 * 8, 4 * 16
+        assert (wsn[offs[2]:offs[2] + 4 * nq].view(np.float32) == host(ref["q_scale"]).ravel()).all()
+        assert (wsn[offs[3]:offs[3] + 4 * nk].view(np.float32) == host(ref["k_scale"]).ravel()).all()
+        if pv_mode == "fp8":
+            _, vs = sage.sage_quant_v_fp8(v)
+            assert (wsn[offs[6]:offs[6] + 4 * 512].view(np.float32) == host(vs).ravel()).all()
+
+
+def test_varlen_small_all_rows():
+    lens = [1, 63, 64, 65, 130, 0, 257]
+    for d in (64, 128):
+        for causal in (False, True):
+            for pv_mode in ("fp16", "fp8"):
+                say(f"case varlen small d={d} causal={causal} pv={pv_mode}")
+                x = workloads.generate_custom(300 + d, 0, 2, 0, d, k_bias=3.0, lengths=lens)
+                cu = dev(x.cu_seqlens)
+                mx = max(lens)
+                o = host(sage.sage_attn_varlen_fwd(dev(x.q), dev(x.k), dev(x.v), cu, mx, is_causal=causal,
+                                                   pv_mode=pv_mode))
+                quant = O.quant_qk_varlen(x.q, x.k, x.cu_seqlens)
+                got = {k2: host(v2) for k2, v2 in sage.sage_quant_qk(dev(x.q), dev(x.k), cu_seqlens=cu,
+                                                                     max_seqlen=mx).items()}
+                assert (got["q_int8"] == quant["q_int8"]).all() and (got["k_int8"] == quant["k_int8"]).all()
+                for i, n in enumerate(lens):
+                    if n == 0:
+                        continue
+                    a = int(x.cu_seqlens[i])
+                    nq, nk = -(-n // 128), -(-n // 64)
+                    assert (got["q_scale"][i, :, :nq].view(np.uint32) == quant["q_scale"][i, :, :nq].view(np.uint32)).all()
+                    assert (got["k_scale"][i, :, :nk].view(np.uint32) == quant["k_scale"][i, :, :nk].view(np.uint32)).all()
+                    assert (got["k_mean"][i].view(np.uint32) == quant["k_mean"][i].view(np.uint32)).all()
+                    for h in range(2):
+                        qi, qs, ki, ks = O.head_views_varlen(quant, x.cu_seqlens, i, h)
+                        vv = x.v[h, a:a + n]
+                        rows = np.arange(n)
+                        if pv_mode == "fp8":
+                            vc, vs = O.quant_v_fp8(vv)
+                            o1 = O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs)
+                        else:
+                            o1 = O.sage_attention_rows(qi, qs, ki, ks, vv, rows, causal, "fp16")
+                        o2 = O.sdpa_fp64_rows(x.q[h, a:a + n], x.k[h, a:a + n], vv, rows, causal)
+                        check_out(o[h, a:a + n], o1, o2, f"varlen seq={i} n={n} h={h}")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads: whole-tensor bit-exact quantisation, sampled output rows
+# ---------------------------------------------------------------------------
+def _sample_rows(n, rng, k=48):
+    return np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, n - 1], rng.choice(n, size=min(n, k), replace=False)]))
+
+
+@pytest.mark.parametrize("name", ["tiny", "llm_prefill", "video_dit", "video_dit_biasx20", "long_fp8", "seq16k"])
+def test_dense_workload(name):
+    w = workloads.get(name)
+    say(f"case workload {name} {w.description}")
+    x = inputs(name)
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    got = {k2: host(v2) for k2, v2 in sage.sage_quant_qk(q, k).items()}
+    ref = O.quant_qk_dense(x.q, x.k)
+    for key in ("q_int8", "k_int8", "q_scale", "k_scale", "k_mean"):
+        assert (got[key].view(np.uint8) == ref[key].view(np.uint8)).all(), key
+    say(f"{name}: quantisation bit-exact over {x.q.size} elements")
+    vc = vs = None
+    if w.pv_mode == "fp8":
+        gc, gs = sage.sage_quant_v_fp8(v)
+        vc, vs = O.quant_v_fp8(x.v)
+        assert (host(gs).view(np.uint32) == vs.view(np.uint32)).all()
+        assert (host(gc) == vc).all()
+        say(f"{name}: e4m3 V bit-exact")
+    del got
+    o = host(sage.sage_attn_fwd(q, k, v, is_causal=w.causal, pv_mode=w.pv_mode))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(w.seed + 5)
+    B, H, N, d = x.q.shape
+    heads = [(0, 0), (B - 1, H - 1)] + [(int(rng.integers(B)), int(rng.integers(H))) for _ in range(2)]
+    if name == "tiny":
+        heads = [(0, 0), (0, 1)]
+    for b, h in heads:
+        rows = np.arange(N) if name == "tiny" else _sample_rows(N, rng)
+        qi, qs, ki, ks = O.head_views_dense(ref, b, h)
+        if w.pv_mode == "fp8":
+            o1 = O.sage_attention_rows(qi, qs, ki, ks, vc[b, h], rows, w.causal, "fp8", vs[b, h])
+        else:
+            o1 = O.sage_attention_rows(qi, qs, ki, ks, x.v[b, h], rows, w.causal, "fp16")
+        o2 = O.sdpa_fp64_rows(x.q[b, h], x.k[b, h], x.v[b, h], rows, w.causal)
+        floor = COS_O2
+        if name == "video_dit":
+            floor = min(COS_O2, cos(o1, o2) - 1e-4)
+        check_out(o[b, h, rows], o1, o2, f"{name} b={b} h={h}", floor)
+    # int32 tiles of this workload, computed by the attention kernel's QKᵀ code
+    nq, nk = -(-N // 128), -(-N // 64)
+    tl = np.array([(int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(nq)), int(rng.integers(nk)))
+                   for _ in range(64)], np.int32)
+    tiles = host(sage.sage_test_qk_tiles(dev(ref["q_int8"]), dev(ref["k_int8"]), dev(tl)))
+    for t, (b, h, qb, kb) in enumerate(tl.tolist()):
+        want = O.qk_int(ref["q_int8"][b, h, qb * 128:(qb + 1) * 128], ref["k_int8"][b, h, kb * 64:(kb + 1) * 64])
+        assert (tiles[t][:want.shape[0], :want.shape[1]] == want).all(), (b, h, qb, kb)
+
+
+def test_varlen_workload():
+    w = workloads.get("varlen")
+    say(f"case workload varlen {w.description}")
+    x = inputs("varlen")
+    cu = dev(x.cu_seqlens)
+    mx = int(x.lengths.max())
+    q, k, v = dev(x.q), dev(x.k), dev(x.v)
+    got = {k2: host(v2) for k2, v2 in sage.sage_quant_qk(q, k, cu_seqlens=cu, max_seqlen=mx).items()}
+    ref = O.quant_qk_varlen(x.q, x.k, x.cu_seqlens)
+    assert (got["q_int8"] == ref["q_int8"]).all() and (got["k_int8"] == ref["k_int8"]).all()
+    for i, n in enumerate(x.lengths.tolist()):
+        nq, nk = -(-n // 128), -(-n // 64)
+        assert (got["q_scale"][i, :, :nq].view(np.uint32) == ref["q_scale"][i, :, :nq].view(np.uint32)).all()
+        assert (got["k_scale"][i, :, :nk].view(np.uint32) == ref["k_scale"][i, :, :nk].view(np.uint32)).all()
+        assert (got["k_mean"][i].view(np.uint32) == ref["k_mean"][i].view(np.uint32)).all()
+    say("varlen: quantisation bit-exact")
+    o = host(sage.sage_attn_varlen_fwd(q, k, v, cu, mx, is_causal=True))
+    rng = np.random.default_rng(w.seed + 5)
+    for i in [0, int(np.argmax(x.lengths)), int(np.argmin(x.lengths)), 7]:
+        h = int(rng.integers(w.H))
+        n = int(x.lengths[i])
+        a = int(x.cu_seqlens[i])
+        rows = _sample_rows(n, rng)
+        qi, qs, ki, ks = O.head_views_varlen(ref, x.cu_seqlens, i, h)
+        o1 = O.sage_attention_rows(qi, qs, ki, ks, x.v[h, a:a + n], rows, True, "fp16")
+        o2 = O.sdpa_fp64_rows(x.q[h, a:a + n], x.k[h, a:a + n], x.v[h, a:a + n], rows, True)
+        check_out(o[h, a + rows], o1, o2, f"varlen seq={i} n={n} h={h}")
