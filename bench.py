@@ -71,7 +71,7 @@ def measured_traffic(workload):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, x, budget_s=12.0):
+def cpu_baseline(w, x, budget_s=15.0):
     """Time the oracle (as it stands) on a bounded sample: the whole
     quantisation of one head plus attention rows of that head, growing the row
     count until the budget is spent.  Scaled to effective TOPS."""
@@ -82,37 +82,44 @@ def cpu_baseline(w, x, budget_s=12.0):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    if w.varlen:
-        a, b = int(x.cu_seqlens[0]), int(x.cu_seqlens[1])
-        q, k, v = x.q[0, a:b], x.k[0, a:b], x.v[0, a:b]
-    else:
-        q, k, v = x.q[0, 0], x.k[0, 0], x.v[0, 0]
-    n, d = q.shape
-    t0 = time.perf_counter()
-    quant = O.quant_qk_dense(q[None, None], k[None, None])
-    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
-    if w.pv_mode == "fp8":
-        vc, vs = O.quant_v_fp8(v)
-    t_quant = time.perf_counter() - t0
-    rows_done, ops, t_attn = 0, 0.0, 0.0
+    def head(i):
+        if w.varlen:
+            a, b = int(x.cu_seqlens[0]), int(x.cu_seqlens[1])
+            return x.q[i, a:b], x.k[i, a:b], x.v[i, a:b]
+        return x.q[0, i], x.k[0, i], x.v[0, i]
+
     rng = np.random.default_rng(0)
-    chunk = 128
-    while t_attn + t_quant < budget_s and rows_done < n:
-        rows = np.sort(rng.choice(n, size=min(chunk, n), replace=False))
-        t1 = time.perf_counter()
+    chunk = 256
+    t_total, ops, rows_done, heads = 0.0, 0.0, 0, 0
+    while t_total < budget_s and heads < w.H:
+        q, k, v = head(heads)
+        n, d = q.shape
+        t0 = time.perf_counter()
+        quant = O.quant_qk_dense(q[None, None], k[None, None])
+        qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
         if w.pv_mode == "fp8":
-            O.sage_attention_rows(qi, qs, ki, ks, vc, rows, w.causal, "fp8", vs)
-        else:
-            O.sage_attention_rows(qi, qs, ki, ks, v, rows, w.causal, "fp16")
-        t_attn += time.perf_counter() - t1
-        keys = (rows + 1).sum() if w.causal else len(rows) * n
-        ops += 4.0 * keys * d
-        rows_done += len(rows)
-    # the quantisation is charged in proportion to the rows covered
-    t = t_attn + t_quant * rows_done / n
-    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
-            "sample": f"one head ({n} tokens, d={d}): quantisation of the head plus {rows_done} query rows "
-                      f"of attention; {t:.1f} s of CPU time"}
+            vc, vs = O.quant_v_fp8(v)
+        t_quant = time.perf_counter() - t0
+        order = rng.permutation(n)
+        done, t_attn = 0, 0.0
+        while t_total + t_quant + t_attn < budget_s and done < n:
+            rows = np.sort(order[done:done + chunk])
+            t1 = time.perf_counter()
+            if w.pv_mode == "fp8":
+                O.sage_attention_rows(qi, qs, ki, ks, vc, rows, w.causal, "fp8", vs)
+            else:
+                O.sage_attention_rows(qi, qs, ki, ks, v, rows, w.causal, "fp16")
+            t_attn += time.perf_counter() - t1
+            keys = (rows + 1).sum() if w.causal else len(rows) * n
+            ops += 4.0 * keys * d
+            done += len(rows)
+        # the head's quantisation is charged in proportion to the rows covered
+        t_total += t_attn + t_quant * done / n
+        rows_done += done
+        heads += 1
+    return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": int(cores), "kind": "oracle",
+            "sample": f"{heads} head(s) of {n} tokens, d={d}: per-head quantisation plus {rows_done} query rows "
+                      f"of attention; {t_total:.1f} s of CPU time"}
 
 
 def main():
@@ -122,6 +129,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
@@ -133,6 +142,16 @@ def main():
 
     import quantized_attention_quant_amd as sage
     import workloads
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 3}), flush=True)
+        return
 
     w = workloads.get(args.workload)
     log(f"bench: workload {w.name}: {w.description}")

@@ -12,9 +12,11 @@
 //   * causal mask (deepseek.csdn.net post: sageattn with is_causal=True).
 //
 // Design (CDNA4, 64-lane waves):
-//   * One workgroup = 4 waves = 128 queries = one Q scale block; each wave owns
-//     32 queries.  Keys are walked in 64-key tiles (= one K scale block), so
-//     every tile pair has a single scalar δQ·δK.
+//   * One workgroup = 8 waves = 256 queries (two Q scale blocks), each wave
+//     owning 32 queries; two waves per SIMD, so one wave's MFMAs run while the
+//     other's softmax occupies the VALU.  Keys are walked in 64-key tiles
+//     (= one K scale block), so every tile and Q block pair has one scalar
+//     δQ·δK.  Every K̂/V tile streamed into LDS serves 256 queries.
 //   * Sᵀ = K̂·Q̂ᵀ on v_mfma_i32_32x32x32_i8: A = K̂ tile from LDS, B = the
 //     wave's Q̂ held in VGPRs.  The 32x32 output puts one query per lane
 //     (lanes l and l+32 share query l%32, each holding 16 of every 32 keys),
@@ -22,17 +24,19 @@
 //     output rescale α is a per-lane scalar.
 //   * The int32 accumulator starts at the bit pattern of 1.5·2^23: since
 //     |Q̂K̂ᵀ| <= 128·127² < 2^22, the result read as fp32 is exactly
-//     1.5·2^23 + acc, so dequantisation is one FMA per score:
-//     s·log2e - m = fma(F, c, -(1.5·2^23·c + m)) with c = δQ·δK·log2e.
+//     1.5·2^23 + acc, so no int->float conversion is needed.
 //   * PV as Oᵀ = Vᵀ·Pᵀ: the softmax output in the S layout is directly the B
 //     operand; V comes pre-packed (pre-pass) in A-operand order, so LDS reads
 //     are contiguous 16/32-byte lane vectors.  FP16: v_mfma_f32_32x32x16_f16.
 //     FP8: v_mfma_f32_32x32x64_f8f6f4 contracts exactly one 64-key tile.
-//   * K̂ and V tiles are double-buffered in LDS with one barrier per tile; the
-//     K̂ rows use an XOR swizzle of their 16-byte chunks so that the 8 lanes
-//     served together read 8 distinct bank groups.
-//   * Workgroup ids are remapped so that one XCD runs consecutive q-blocks of
-//     the same head (K̂/V reuse in that XCD's L2); heavier causal blocks go
+//   * K̂ and V tiles stream into a 3-stage LDS ring with buffer_load ... lds
+//     (no staging registers; out-of-range K̂ rows read as zero through the
+//     buffer descriptor's size).  Tile t+2 is requested while tile t is being
+//     consumed, so each tile has two iterations to arrive; one barrier per tile.
+//   * The K̂ rows in LDS use an XOR swizzle of their 16-byte chunks so that the
+//     8 lanes served together read 8 distinct bank groups.
+//   * Workgroup ids are remapped so that one XCD runs consecutive query blocks
+//     of the same head (K̂/V reuse in that XCD's L2); heavier causal blocks go
 //     first.
 #include "sage_common.h"
 #include "sage_internal.h"
@@ -43,6 +47,27 @@ constexpr float kMagicF = 12582912.0f;  // 1.5 * 2^23
 constexpr int kMagicI = 0x4B400000;     // its fp32 bit pattern
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2E4M3Max = 8.807354922057604f;  // log2(448)
+// FP16 PV: the running max used as the exponent reference is only moved when
+// a row's max exceeds it by more than this (log2 units), so p <= 2^8 and the
+// output rescale is rare.  Softmax does not depend on the reference and fp16
+// rounding is relative, so this changes nothing but rounding.
+constexpr float kLazyRescale = 8.0f;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kStages = 3;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+template <int D, bool FP8, int NT = kThreads>
+struct TileGeom {
+  static constexpr int KBYTES = kKBlock * D;                    // K̂ tile, int8
+  static constexpr int VBYTES = kKBlock * D * (FP8 ? 1 : 2);    // packed V tile
+  static constexpr int KCHUNKS = KBYTES / 16;
+  static constexpr int VCHUNKS = VBYTES / 16;
+  static constexpr int KI = KCHUNKS / NT;                       // DMA instructions per wave
+  static constexpr int VI = VCHUNKS / NT;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static_assert(KI * NT == KCHUNKS && VI * NT == VCHUNKS, "tile must split evenly over the waves");
+};
 
 // 16-byte chunk index of K̂ tile row r, chunk c inside LDS (XOR swizzle).
 template <int D>
@@ -52,50 +77,80 @@ __device__ __forceinline__ int k_lds_chunk(int r, int c) {
   return r * CPR + (c ^ ((r >> RSH) & (CPR - 1)));
 }
 
-template <int D>
-struct KTileRegs {
-  static constexpr int N = kKBlock * D / 16 / kThreads;  // 16-byte chunks per thread
-  v4i r[N];
-};
-
-template <int D, bool FP8>
-struct VTileRegs {
-  static constexpr int BYTES = kKBlock * D * (FP8 ? 1 : 2);
-  static constexpr int N = BYTES / 16 / kThreads;
-  v4i r[N];
-};
-
-// Global -> registers for K̂ rows [k0, k0+64) of a head-sequence (zeros past n).
-template <int D>
-__device__ __forceinline__ void load_k_tile(KTileRegs<D>& kr, const int8_t* __restrict__ kbase, int k0, int n) {
+// Request K̂ tile t (rows 64t..64t+63 of the head-sequence, zeros past its end)
+// and packed V tile t into one LDS stage.  kbase/kbytes and vbase/vbytes bound
+// the head-sequence's K̂ rows and packed V tiles; reads past them return zero.
+// Lane i of a DMA instruction lands at the instruction's LDS base + 16·i, so
+// each lane fetches the global chunk that belongs at its swizzled position.
+template <int D, bool FP8, int NT = kThreads>
+__device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const void* vbase, int vbytes, int t,
+                                           char* stage, int w, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)  // the buffer-descriptor type exists only for the GPU target
+  using G = TileGeom<D, FP8, NT>;
   constexpr int CPR = D / 16;
+  constexpr int RSH = (CPR == 8) ? 0 : 1;
+  const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), (short)0, kbytes,
+                                                                      kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), (short)0, vbytes,
+                                                                      kBufferFlags);
 #pragma unroll
-  for (int i = 0; i < KTileRegs<D>::N; ++i) {
-    const int idx = threadIdx.x + kThreads * i;
-    const int r = idx / CPR, c = idx % CPR;
-    kr.r[i] = (k0 + r < n) ? *reinterpret_cast<const v4i*>(kbase + (int64_t)(k0 + r) * D + c * 16)
-                           : v4i{0, 0, 0, 0};
+  for (int j = 0; j < G::KI; ++j) {
+    const int base = (w * G::KI + j) * 64;  // wave-uniform chunk index
+    const int p = base + lane;
+    const int r = p / CPR;
+    const int c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(stage + base * 16), 16,
+                                             (t * kKBlock + r) * D + c * 16, 0, 0, 0);
   }
-}
-template <int D>
-__device__ __forceinline__ void store_k_tile(const KTileRegs<D>& kr, v4i* __restrict__ lds) {
-  constexpr int CPR = D / 16;
 #pragma unroll
-  for (int i = 0; i < KTileRegs<D>::N; ++i) {
-    const int idx = threadIdx.x + kThreads * i;
-    lds[k_lds_chunk<D>(idx / CPR, idx % CPR)] = kr.r[i];
+  for (int j = 0; j < G::VI; ++j) {
+    const int base = (w * G::VI + j) * 64;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + base * 16), 16,
+                                             t * G::VBYTES + (base + lane) * 16, 0, 0, 0);
   }
+#endif
 }
-template <int D, bool FP8>
-__device__ __forceinline__ void load_v_tile(VTileRegs<D, FP8>& vr, const uint8_t* __restrict__ tile) {
-#pragma unroll
-  for (int i = 0; i < VTileRegs<D, FP8>::N; ++i)
-    vr.r[i] = *reinterpret_cast<const v4i*>(tile + (int64_t)(threadIdx.x + kThreads * i) * 16);
+
+// Workgroup barrier without a workgroup-scope memory fence.  __syncthreads()
+// makes every wave wait for all its outstanding vector-memory loads — the tile
+// DMA in flight included — before the barrier.  Here each wave that issued tile
+// DMA waits for exactly the tile the next phase reads (wait_dma).  The
+// wavefront-scope fences emit no wait; they keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void barrier_only() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-template <int D, bool FP8>
-__device__ __forceinline__ void store_v_tile(const VTileRegs<D, FP8>& vr, v4i* __restrict__ lds) {
-#pragma unroll
-  for (int i = 0; i < VTileRegs<D, FP8>::N; ++i) lds[threadIdx.x + kThreads * i] = vr.r[i];
+
+// Wait until at most OUTSTANDING of this wave's vector-memory loads are in
+// flight (tile DMA completes in issue order).
+template <int OUTSTANDING>
+__device__ __forceinline__ void wait_dma() {
+  static_assert(OUTSTANDING >= 0 && OUTSTANDING < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | OUTSTANDING);
+}
+
+template <int OUTSTANDING>
+__device__ __forceinline__ void wait_dma_and_sync() {
+  wait_dma<OUTSTANDING>();
+  barrier_only();
+}
+
+// Uniform loads of read-only scales through the scalar data cache (SMEM), so
+// they never wait behind the vector-memory counter the tile DMA uses.
+__device__ __forceinline__ float load_uniform(const float* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) float*)p)[i];
+}
+
+// max / sum over the two lanes that hold the same query row (l and l ^ 32).
+__device__ __forceinline__ float pair_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
 
 // The wave's Q̂ as the B operand of Sᵀ = K̂Q̂ᵀ: lane holds query r32, channels
@@ -109,194 +164,315 @@ __device__ __forceinline__ void load_q_frags(v4i (&qf)[D / 32], const int8_t* __
                         : v4i{0, 0, 0, 0};
 }
 
-// Sᵀ for one 64-key tile: S[s] covers keys 32s..32s+31; lane (r32, g) reg i
-// holds key 32s + 8(i/4) + 4g + i%4 of query r32, as magic + Σ q̂·k̂.
+// K̂ fragments of one 64-key tile (A operand of Sᵀ = K̂Q̂ᵀ): kf[s][ks] is the
+// 16 bytes of key 32s + r32, channels 32ks + 16g .. +15.
 template <int D>
-__device__ __forceinline__ void qk_tile(const v4i* __restrict__ lds_k, const v4i (&qf)[D / 32], v16i (&S)[2],
-                                        int r32, int g) {
+__device__ __forceinline__ void load_k_frags(const v4i* __restrict__ lds_k, v4i (&kf)[2][D / 32], int r32, int g) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) kf[s][ks] = lds_k[k_lds_chunk<D>(32 * s + r32, 2 * ks + g)];
+}
+
+// Sᵀ of one 32-query half for one 64-key tile: S[s] covers keys 32s..32s+31;
+// lane (r32, g) reg i holds key 32s + 8(i/4) + 4g + i%4 of query r32, as
+// magic + Σ q̂·k̂.
+template <int D>
+__device__ __forceinline__ void qk_half(const v4i (&kf)[2][D / 32], const v4i (&qf)[D / 32], v16i (&S)[2]) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     v16i acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = kMagicI;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const v4i a = lds_k[k_lds_chunk<D>(32 * s + r32, 2 * ks + g)];
-      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qf[ks], acc, 0, 0, 0);
-    }
+    for (int ks = 0; ks < D / 32; ++ks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[s][ks], qf[ks], acc, 0, 0, 0);
     S[s] = acc;
   }
 }
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
 
+// Scores of a half as fp32 (magic-biased); with MASKED, keys past n or (causal)
+// after the row's query become 0, below every real value (>= 2^23).  Returns
+// the row max over both lanes of the row.
+template <bool CAUSAL, bool MASKED>
+__device__ __forceinline__ float scores(const v16i (&S)[2], float (&F)[2][16], int k0, int n, int qrow, int gg) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // read the element by value first: a bit cast of an ext-vector element
+      // lvalue compiles to a read of element 0
+      const int bits = S[s][i];
+      float f = __int_as_float(bits);
+      if (MASKED) {
+        const int key = k0 + 32 * s + 8 * (i >> 2) + 4 * gg + (i & 3);
+        const bool vis = key < n && (!CAUSAL || key <= qrow);
+        f = vis ? f : 0.f;
+      }
+      F[s][i] = f;
+    }
+  float mx = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = max3f(mx, F[s][i], F[s][i + 1]);
+  return pair_max(mx);
+}
+
+__device__ __forceinline__ float tile_max(float mx, float c2) {
+  return (mx == 0.f) ? -__builtin_inff() : (mx - kMagicF) * c2;
+}
+
+// FP16 PV: p = 2^(F·c - K), K = fl(1.5·2^23·c + m_run) — one FMA per score.
+// The rounding of K shifts a row-tile's exponents by <= ulp(K)/2, a common
+// factor on its p and on its share of l.  P is packed as four B operands.
+template <bool MASKED>
+__device__ __forceinline__ float exp_pack_fp16(const float (&F)[2][16], float c2, float m_ref, v8h (&pk)[4]) {
+  const float kb = __builtin_fmaf(kMagicF, c2, m_ref);
+  float lsum = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    const int s = kc >> 1, hh = kc & 1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = F[s][8 * hh + j];
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(f, c2, -kb));
+      if (MASKED) p = (f == 0.f) ? 0.f : p;
+      lsum += p;
+      pk[kc][j] = (_Float16)p;
+    }
+  }
+  return lsum;
+}
+
+// FP8 PV: the e4m3 codes of 448·p follow the running max itself (the schedule
+// the method fixes): p·448 = 2^((F - mx)·c + (m_tile - m) + log2 448), with
+// F - mx exact (both in [2^23, 2^24)); p·448 <= 448·2^(2^-20) < 464, so the
+// conversion cannot overflow.  P is packed as one 32-byte B operand.
+template <bool MASKED>
+__device__ __forceinline__ float exp_pack_fp8(const float (&F)[2][16], float mx, float c2, float cterm, v8i& pk) {
+  float lsum = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int s = q >> 2, i0 = 4 * (q & 3);
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float f = F[s][i0 + j];
+      float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f - mx, c2, cterm));
+      if (MASKED) e = (f == 0.f) ? 0.f : e;
+      lsum += e;
+      p[j] = e;
+    }
+    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    pk[q] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
+  }
+  return lsum;
+}
+
+// O += P·V for one group of 32 queries.  FP8: level 1 (one tile's 64 keys)
+// and level 2 (the running output) are one fp32 MFMA per d tile.
+template <int D, bool FP8>
+__device__ __forceinline__ void pv_tile(const char* __restrict__ vstage, int lane, const v8h (&pk16)[4],
+                                        const v8i& pk8, v16f (&O)[D / 32]) {
+  constexpr int DT = D / 32;
+  if (!FP8) {
+    const v8h* lv = reinterpret_cast<const v8h*>(vstage);
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lv[(kc * DT + dt) * 64 + lane], pk16[kc], O[dt], 0, 0, 0);
+  } else {
+    const v8i* lv = reinterpret_cast<const v8i*>(vstage);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lv[dt * 64 + lane], pk8, O[dt], 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// Row sum of packed fp16 p: fp32 accumulation of the rounded values that PV
+// applies, two per instruction.
+__device__ __forceinline__ float sum_pk(const v8h (&pk)[4]) {
+  const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
+  float s = 0.f;
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      const v2h pr = {pk[kc][j], pk[kc][j + 1]};
+      s = __builtin_amdgcn_fdot2(pr, one, s, false);
+    }
+  return s;
+}
+
+template <int D>
+__device__ __forceinline__ void rescale_o(v16f (&O)[D / 32], float& l_run, float alpha) {
+  l_run *= alpha;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[dt][i] *= alpha;
+}
+
+// Per-wave state of the 32-query attention pipeline.
+template <int D, bool FP8>
+struct WaveCtx {
+  v4i qf[D / 32];   // Q̂ B operand
+  v16f O[D / 32];   // Oᵀ accumulator (d tiles of 32)
+  v16i S[2];        // Sᵀ of the current tile
+  v8h pk16[4];      // P of the previous tile (fp16 PV)
+  v8i pk8;          // P of the previous tile (fp8 PV)
+  float m_run;      // exponent reference (log2 units)
+  float l_run;      // this lane's share of the row sum
+};
+
+// Softmax phase of one tile: scores -> P (kept for the next matrix phase), row
+// statistics and, when needed, the output rescale.  MASKED: keys past n or
+// (causal) after the row's query are excluded.
+template <int D, bool FP8, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2, int k0, int n, int qrow, int gg) {
+  float F[2][16];
+  const float mx = scores<CAUSAL, MASKED>(c.S, F, k0, n, qrow, gg);
+  const float mt = tile_max(mx, c2);
+  if (!FP8) {
+    // lazy reference: moves only when a row max passed it by more than kLazyRescale
+    if (__any(mt > c.m_run + kLazyRescale)) {
+      float m_new = __builtin_fmaxf(c.m_run, mt);
+      m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
+      rescale_o<D>(c.O, c.l_run, __builtin_amdgcn_exp2f(c.m_run - m_new));
+      c.m_run = m_new;
+    }
+    exp_pack_fp16<MASKED>(F, c2, c.m_run, c.pk16);
+    c.l_run += sum_pk(c.pk16);
+  } else {
+    float m_new = __builtin_fmaxf(c.m_run, mt);
+    m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(c.m_run - m_new);
+    const float lsum = exp_pack_fp8<MASKED>(F, mx, c2, (mt - m_new) + kLog2E4M3Max, c.pk8);
+    if (__any(alpha != 1.f))
+      rescale_o<D>(c.O, c.l_run, alpha);
+    c.m_run = m_new;
+    c.l_run += lsum;
+  }
+}
+
+// Workgroup: 8 waves x 32 queries = 256 queries (two Q scale blocks), two waves
+// per SIMD.  Waves 0-3 (group A) and 4-7 (group B) run the same pipeline one
+// phase apart — matrix phase (PV of tile t-1, QKᵀ of tile t) then softmax
+// phase (tile t), a workgroup barrier between phases — so on every SIMD one
+// wave's MFMAs overlap the other wave's softmax.  Group A streams the tiles.
+constexpr int kAttnWaves = 8;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kAttnRows = 32 * kAttnWaves;
+constexpr int kRingStages = 4;  // tile t+2 loads while group B may still read tile t-1
+
 template <int D, bool FP8, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads), amdgpu_waves_per_eu(2, 2)))
+void attn_fwd_kernel(AttnArgs a) {
   constexpr int DT = D / 32;  // 32-wide d tiles of the output
-  using VR = VTileRegs<D, FP8>;
-  __shared__ v4i lds_k[2][kKBlock * D / 16];
-  __shared__ v4i lds_v[2][VR::BYTES / 16];
+  using G = TileGeom<D, FP8, kThreads>;  // tiles are streamed by the 4 waves of group A
+  __shared__ __attribute__((aligned(1024))) char smem[kRingStages * G::STAGE];
 
   const SeqGeom& g = a.g;
   const int nqb = ceil_div(g.N, kQBlock);
   const int nkb = ceil_div(g.N, kKBlock);
+  const int nwb = ceil_div(g.N, kAttnRows);
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int qb = nqb - 1 - logical % nqb;  // heavy (late) causal blocks first
-  const int hb = logical / nqb;
+  const int wb = nwb - 1 - logical % nwb;  // heavy (late) causal blocks first
+  const int hb = logical / nwb;
   const int h = hb / g.B, b = hb % g.B;
   int64_t row0;
   int n;
   hs_rows(g, b, h, row0, n);
-  const int q0 = qb * kQBlock;
+  const int q0 = wb * kAttnRows;
   if (q0 >= n) return;
 
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r32 = lane & 31, gg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, gg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = w < kAttnWaves / 2;  // group A
   const int64_t hs = (int64_t)b * g.H + h;
-  const int qrow = q0 + 32 * w + r32;
-  const int wq_lo = q0 + 32 * w;
+  const int wq_lo = q0 + 32 * w;  // first query of the wave
+  const int qrow = wq_lo + r32;
   const int wq_hi = min(wq_lo + 31, n - 1);
   const bool wave_rows = wq_lo < n;
 
-  v4i qf[DT];
-  load_q_frags<D>(qf, a.q + row0 * D, qrow, n, gg);
-  const float dq = a.q_scale[hs * nqb + qb];
-  const float* __restrict__ ksc = a.k_scale + hs * nkb;
-  const int8_t* __restrict__ kbase = a.k + row0 * D;
-  const uint8_t* __restrict__ vbase = a.v_packed + vtile_index(g, b, h, 0) * VR::BYTES;
-
-  const int kend = CAUSAL ? min(n, q0 + kQBlock) : n;
+  const int kend = CAUSAL ? min(n, q0 + kAttnRows) : n;
   const int ntiles = ceil_div(kend, kKBlock);
+  const int8_t* kbase = a.k + row0 * D;
+  const int kbytes = n * D;
+  const uint8_t* vbase = a.v_packed + vtile_index(g, b, h, 0) * G::VBYTES;
+  const int vbytes = ceil_div(n, kKBlock) * G::VBYTES;
+  constexpr int L = G::KI + G::VI;  // DMA instructions per group-A wave per tile
 
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
-  v16f O[DT];
+  WaveCtx<D, FP8> c;
+  load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
+  const float dq = load_uniform(a.q_scale, hs * nqb + wq_lo / kQBlock);
+  const float* __restrict__ ksc = a.k_scale + hs * nkb;
+  c.m_run = -__builtin_inff();
+  c.l_run = 0.f;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) O[dt][i] = 0.f;
+    for (int i = 0; i < 16; ++i) c.O[dt][i] = 0.f;
 
-  {
-    KTileRegs<D> kr;
-    VR vr;
-    load_k_tile<D>(kr, kbase, 0, n);
-    load_v_tile<D, FP8>(vr, vbase);
-    store_k_tile<D>(kr, lds_k[0]);
-    store_v_tile<D, FP8>(vr, lds_v[0]);
+  if (lead) {
+    issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, 0, smem, w, lane);
+    if (ntiles > 1) {
+      issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, 1, smem + G::STAGE, w, lane);
+      wait_dma<L>();  // tile 0 landed
+    } else {
+      wait_dma<0>();
+    }
   }
-  __syncthreads();
+  barrier_only();
+  if (!lead) barrier_only();  // group B runs one phase behind
 
+  // tiles this wave takes part in: 0..nact-1 (causal: keys up to its last query)
+  const int nact = !wave_rows ? 0 : CAUSAL ? min(ntiles, wq_hi / kKBlock + 1) : ntiles;
   for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    const bool next = t + 1 < ntiles;
-    KTileRegs<D> kr;
-    VR vr;
-    if (next) {
-      load_k_tile<D>(kr, kbase, (t + 1) * kKBlock, n);
-      load_v_tile<D, FP8>(vr, vbase + (int64_t)(t + 1) * VR::BYTES);
-    }
     const int k0 = t * kKBlock;
-    if (wave_rows && (!CAUSAL || k0 <= wq_hi)) {
-      v16i S[2];
-      qk_tile<D>(lds_k[buf], qf, S, r32, gg);
-      const float c2 = dq * ksc[t] * kLog2e;
+    const bool act = t < nact;
+    const bool have_p = t > 0 && t <= nact;  // P of tile t-1 is pending its PV
+    // ---- matrix phase: PV of tile t-1, QKᵀ of tile t
+    __builtin_amdgcn_s_setprio(1);
+    if (lead && t + 2 < ntiles)
+      issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, t + 2, smem + ((t + 2) % kRingStages) * G::STAGE, w, lane);
+    if (have_p)
+      pv_tile<D, FP8>(smem + ((t + kRingStages - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, c.pk16, c.pk8,
+                      c.O);
+    if (act) {
+      v4i kf[2][DT];
+      load_k_frags<D>(reinterpret_cast<const v4i*>(smem + (t % kRingStages) * G::STAGE), kf, r32, gg);
+      qk_half<D>(kf, c.qf, c.S);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    barrier_only();
+    // ---- softmax phase: tile t
+    if (act) {
+      const float c2 = dq * load_uniform(ksc, t) * kLog2e;
       const bool full = (k0 + kKBlock <= n) && (!CAUSAL || k0 + kKBlock - 1 <= wq_lo);
-      float F[2][16];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          // read the element by value first: a bit cast of an ext-vector element lvalue
-          // compiles to a read of element 0
-          const int bits = S[s][i];
-          F[s][i] = __int_as_float(bits);
-        }
-      if (!full) {
-        // masked scores -> 0.0f, below every real value (>= 2^23)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * s + 8 * (i >> 2) + 4 * gg + (i & 3);
-            const bool vis = key < n && (!CAUSAL || key <= qrow);
-            F[s][i] = vis ? F[s][i] : 0.f;
-          }
-      }
-      float mx = 0.f;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int i = 0; i < 16; i += 2) mx = max3f(mx, F[s][i], F[s][i + 1]);
-      mx = __builtin_fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_tile = (mx == 0.f) ? -__builtin_inff() : (mx - kMagicF) * c2;
-      float m_new = __builtin_fmaxf(m_run, m_tile);
-      m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      // FP16 PV: one FMA per score, p = 2^(F·c - K) with K = fl(1.5·2^23·c + m).  The
-      // rounding of K shifts a whole row-tile by <= ulp(K)/2 in the exponent (a common
-      // factor on that tile's p and its share of l); fp16 P rounding is relative, so its
-      // codes do not depend on it.
-      // FP8 PV: the e4m3 codes of 448·p must follow the running max itself, so the
-      // exponent is taken from the exact difference F - max (both in [2^23, 2^24)):
-      // p·448 = 2^((F - mx)·c + (m_tile - m) + log2 448).
-      const float kb = __builtin_fmaf(kMagicF, c2, m_new);
-      const float cterm = (m_tile - m_new) + kLog2E4M3Max;
-      float P[2][16];
-      float lsum = 0.f;
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float arg = FP8 ? __builtin_fmaf(F[s][i] - mx, c2, cterm) : __builtin_fmaf(F[s][i], c2, -kb);
-          float p = __builtin_amdgcn_exp2f(arg);
-          if (!full) p = (F[s][i] == 0.f) ? 0.f : p;
-          P[s][i] = p;
-          lsum += p;
-        }
-      l_run = alpha * l_run + lsum;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) O[dt][i] *= alpha;
-      }
-      if (!FP8) {
-        const v8h* __restrict__ lv = reinterpret_cast<const v8h*>(lds_v[buf]);
-#pragma unroll
-        for (int kc = 0; kc < 4; ++kc) {
-          const int s = kc >> 1, hh = kc & 1;
-          v8h pk;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) pk[j] = (_Float16)P[s][8 * hh + j];
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-            O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lv[(kc * DT + dt) * 64 + lane], pk, O[dt], 0, 0, 0);
-        }
-      } else {
-        // p·448 <= 448·2^(1e-5) < 464, so the conversion cannot overflow e4m3.
-        v8i pk;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int s = q >> 2, i0 = 4 * (q & 3);
-          int wv = __builtin_amdgcn_cvt_pk_fp8_f32(P[s][i0], P[s][i0 + 1], 0, false);
-          wv = __builtin_amdgcn_cvt_pk_fp8_f32(P[s][i0 + 2], P[s][i0 + 3], wv, true);
-          pk[q] = wv;
-        }
-        const v8i* __restrict__ lv = reinterpret_cast<const v8i*>(lds_v[buf]);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lv[dt * 64 + lane], pk, O[dt], 0, 0, 0, 0, 0, 0);
-      }
+      if (full)
+        softmax_phase<D, FP8, CAUSAL, false>(c, c2, k0, n, qrow, gg);
+      else
+        softmax_phase<D, FP8, CAUSAL, true>(c, c2, k0, n, qrow, gg);
     }
-    if (next) {
-      store_k_tile<D>(kr, lds_k[buf ^ 1]);
-      store_v_tile<D, FP8>(vr, lds_v[buf ^ 1]);
+    if (lead) {
+      // tile t+1 landed before anyone's next matrix phase (tile t+2 may still fly)
+      if (t + 2 < ntiles)
+        wait_dma<L>();
+      else
+        wait_dma<0>();
     }
-    __syncthreads();
+    barrier_only();
   }
+  if (nact == ntiles && ntiles > 0)
+    pv_tile<D, FP8>(smem + ((ntiles - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, c.pk16, c.pk8, c.O);
+  if (lead) barrier_only();  // matches group B's extra barrier
 
   // Epilogue: o = O / l (FP16) or O·δV / l with l holding 448·Σp (FP8).
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(c.l_run);
   if (!wave_rows || qrow >= n) return;
   const float inv = 1.f / l_tot;
   uint16_t* __restrict__ orow = a.o + (row0 + qrow) * D;
@@ -307,9 +483,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
       const int d = 32 * dt + 8 * q4 + 4 * gg;
       float f[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) f[j] = O[dt][4 * q4 + j] * inv;
+      for (int j = 0; j < 4; ++j) f[j] = c.O[dt][4 * q4 + j] * inv;
       if (FP8) {
-        const float4 vs = *reinterpret_cast<const float4*>(a.v_scale + hs * D + d);
+        const float4 vs = *reinterpret_cast<const float4*>(a.v_scale + hs * D + d);  // per-lane d
         f[0] *= vs.x;
         f[1] *= vs.y;
         f[2] *= vs.z;
@@ -317,19 +493,21 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
       }
       v2h lo = {(_Float16)f[0], (_Float16)f[1]};
       v2h hi = {(_Float16)f[2], (_Float16)f[3]};
-      uint2 st;
-      st.x = __builtin_bit_cast(uint32_t, lo);
-      st.y = __builtin_bit_cast(uint32_t, hi);
-      *reinterpret_cast<uint2*>(orow + d) = st;
+      uint2 stv;
+      stv.x = __builtin_bit_cast(uint32_t, lo);
+      stv.y = __builtin_bit_cast(uint32_t, hi);
+      *reinterpret_cast<uint2*>(orow + d) = stv;
     }
 }
 
-// Test hook: the int32 Q̂K̂ᵀ tiles computed by the same device code as above.
+// Test hook: the int32 Q̂K̂ᵀ tiles computed by the same tile DMA and QKᵀ device
+// code as the attention kernel.
 template <int D>
 __global__ __launch_bounds__(kThreads) void qk_tiles_kernel(const int8_t* __restrict__ q, const int8_t* __restrict__ k,
                                                             int B, int H, int N, const int32_t* __restrict__ list,
                                                             int32_t* __restrict__ out) {
-  __shared__ v4i lds_k[kKBlock * D / 16];
+  using G = TileGeom<D, false>;
+  __shared__ __attribute__((aligned(1024))) char smem[G::STAGE];
   const int idx = blockIdx.x;
   const int b = list[4 * idx], h = list[4 * idx + 1], qb = list[4 * idx + 2], kb = list[4 * idx + 3];
   int32_t* o = out + (int64_t)idx * kQBlock * kKBlock;
@@ -338,15 +516,17 @@ __global__ __launch_bounds__(kThreads) void qk_tiles_kernel(const int8_t* __rest
     return;
   }
   const int64_t row0 = ((int64_t)b * H + h) * N;
-  KTileRegs<D> kr;
-  load_k_tile<D>(kr, k + row0 * D, kb * kKBlock, N);
-  store_k_tile<D>(kr, lds_k);
-  __syncthreads();
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, r32 = lane & 31, gg = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, gg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the V half of the stage is not used here: a zero-size range reads zeros
+  issue_tile<D, false>(k + row0 * D, N * D, k, 0, kb, smem, w, lane);
+  wait_dma_and_sync<0>();
   v4i qf[D / 32];
   load_q_frags<D>(qf, q + row0 * D, qb * kQBlock + 32 * w + r32, N, gg);
+  v4i kf[2][D / 32];
+  load_k_frags<D>(reinterpret_cast<const v4i*>(smem), kf, r32, gg);
   v16i S[2];
-  qk_tile<D>(lds_k, qf, S, r32, gg);
+  qk_half<D>(kf, qf, S);
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -357,8 +537,8 @@ __global__ __launch_bounds__(kThreads) void qk_tiles_kernel(const int8_t* __rest
 }
 
 void launch_attn(const AttnArgs& a, bool causal, bool fp8, hipStream_t st) {
-  const int64_t blocks = (int64_t)a.g.B * a.g.H * ceil_div(a.g.N, kQBlock);
-  const dim3 grid((unsigned)blocks), block(kThreads);
+  const int64_t blocks = (int64_t)a.g.B * a.g.H * ceil_div(a.g.N, kAttnRows);
+  const dim3 grid((unsigned)blocks), block(kAttnThreads);
 #define SAGE_ATTN(DD, F8, CS) hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS>), grid, block, 0, st, a)
   if (a.g.d == 128) {
     if (!fp8) { if (causal) SAGE_ATTN(128, false, true); else SAGE_ATTN(128, false, false); }
