@@ -47,11 +47,10 @@ constexpr float kMagicF = 12582912.0f;  // 1.5 * 2^23
 constexpr int kMagicI = 0x4B400000;     // its fp32 bit pattern
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2E4M3Max = 8.807354922057604f;  // log2(448)
-// FP16 PV: the running max used as the exponent reference is only moved when
-// a row's max exceeds it by more than this (log2 units), so p <= 2^8 and the
-// output rescale is rare.  Softmax does not depend on the reference and fp16
-// rounding is relative, so this changes nothing but rounding.
+// FP16 PV: the exponent reference is only moved when a lane's row-tile sum of
+// p exceeds 2^kLazyRescale, so p <= 2^8 and the output rescale is rare.
 constexpr float kLazyRescale = 8.0f;
+constexpr float kLazyLimit = 256.0f;  // 2^kLazyRescale
 constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kStages = 3;
 
@@ -69,12 +68,21 @@ struct TileGeom {
   static_assert(KI * NT == KCHUNKS && VI * NT == VCHUNKS, "tile must split evenly over the waves");
 };
 
-// 16-byte chunk index of K̂ tile row r, chunk c inside LDS (XOR swizzle).
+// 16-byte chunk index of K̂ tile row r, chunk c inside LDS (XOR swizzle).  A
+// 128-bit LDS read serves 16 lanes at a time from 64 banks x 4 bytes = 256
+// bytes; the 16 lanes of a fragment read hold 16 consecutive rows at one chunk
+// column, and 256/D rows share a 256-byte bank line.  XOR-ing the chunk with
+// r / (256/D) gives the 16 lanes 16 distinct 16-byte bank groups.
+template <int D>
+struct KSwizzle {
+  static constexpr int CPR = D / 16;               // chunks per row: 8 (d=128) or 4 (d=64)
+  static constexpr int RSH = (D == 128) ? 1 : 2;   // log2 of rows per 256-byte bank line
+  static __device__ __forceinline__ int chunk(int r, int c) { return c ^ ((r >> RSH) & (CPR - 1)); }
+};
+
 template <int D>
 __device__ __forceinline__ int k_lds_chunk(int r, int c) {
-  constexpr int CPR = D / 16;              // chunks per row: 8 (d=128) or 4 (d=64)
-  constexpr int RSH = (CPR == 8) ? 0 : 1;  // rows sharing a 128-byte bank line
-  return r * CPR + (c ^ ((r >> RSH) & (CPR - 1)));
+  return r * KSwizzle<D>::CPR + KSwizzle<D>::chunk(r, c);
 }
 
 // Request K̂ tile t (rows 64t..64t+63 of the head-sequence, zeros past its end)
@@ -88,7 +96,6 @@ __device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const 
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer-descriptor type exists only for the GPU target
   using G = TileGeom<D, FP8, NT>;
   constexpr int CPR = D / 16;
-  constexpr int RSH = (CPR == 8) ? 0 : 1;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), (short)0, kbytes,
                                                                       kBufferFlags);
   const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), (short)0, vbytes,
@@ -98,7 +105,7 @@ __device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const 
     const int base = (w * G::KI + j) * 64;  // wave-uniform chunk index
     const int p = base + lane;
     const int r = p / CPR;
-    const int c = (p % CPR) ^ ((r >> RSH) & (CPR - 1));
+    const int c = KSwizzle<D>::chunk(r, p % CPR);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(stage + base * 16), 16,
                                              (t * kKBlock + r) * D + c * 16, 0, 0, 0);
   }
@@ -192,65 +199,54 @@ __device__ __forceinline__ void qk_half(const v4i (&kf)[2][D / 32], const v4i (&
 
 __device__ __forceinline__ float max3f(float a, float b, float c) { return __builtin_fmaxf(__builtin_fmaxf(a, b), c); }
 
-// Scores of a half as fp32 (magic-biased); with MASKED, keys past n or (causal)
-// after the row's query become 0, below every real value (>= 2^23).  Returns
-// the row max over both lanes of the row.
-template <bool CAUSAL, bool MASKED>
-__device__ __forceinline__ float scores(const v16i (&S)[2], float (&F)[2][16], int k0, int n, int qrow, int gg) {
+// Masking of a tile that is not fully visible: keys past n or (causal) after
+// the row's query get the bit pattern of -inf in place of the magic-biased
+// score, so they fall out of the row max and give p = 0 below (c > 0).
+constexpr int kNegInfBits = (int)0xFF800000u;
+
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_scores(v16i (&S)[2], int k0, int n, int qrow, int gg) {
+  // lane (r32, g) reg i of S[s] holds key k0 + 4g + (32s + 8(i/4) + i%4)
+  const int lim = (CAUSAL ? min(n - 1, qrow) : n - 1) - k0 - 4 * gg;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      // read the element by value first: a bit cast of an ext-vector element
-      // lvalue compiles to a read of element 0
-      const int bits = S[s][i];
-      float f = __int_as_float(bits);
-      if (MASKED) {
-        const int key = k0 + 32 * s + 8 * (i >> 2) + 4 * gg + (i & 3);
-        const bool vis = key < n && (!CAUSAL || key <= qrow);
-        f = vis ? f : 0.f;
-      }
-      F[s][i] = f;
+      const int off = 32 * s + 8 * (i >> 2) + (i & 3);
+      const int v = S[s][i];
+      S[s][i] = (off <= lim) ? v : kNegInfBits;
     }
-  float mx = 0.f;
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int i = 0; i < 16; i += 2) mx = max3f(mx, F[s][i], F[s][i + 1]);
-  return pair_max(mx);
 }
 
 __device__ __forceinline__ float tile_max(float mx, float c2) {
   return (mx == 0.f) ? -__builtin_inff() : (mx - kMagicF) * c2;
 }
 
-// FP16 PV: p = 2^(F·c - K), K = fl(1.5·2^23·c + m_run) — one FMA per score.
+// FP16 PV: p = 2^(F·c - K), K = fl(1.5·2^23·c + m_ref) — one FMA per score.
 // The rounding of K shifts a row-tile's exponents by <= ulp(K)/2, a common
-// factor on its p and on its share of l.  P is packed as four B operands.
-template <bool MASKED>
+// factor on its p and on its share of l.  P is packed as four B operands; the
+// returned row-tile sum is over the unrounded p, in fp32 adds (dot instructions
+// would share the matrix pipeline and stall behind the other wave's MFMAs).
 __device__ __forceinline__ float exp_pack_fp16(const float (&F)[2][16], float c2, float m_ref, v8h (&pk)[4]) {
   const float kb = __builtin_fmaf(kMagicF, c2, m_ref);
-  float lsum = 0.f;
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
     const int s = kc >> 1, hh = kc & 1;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float f = F[s][8 * hh + j];
-      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(f, c2, -kb));
-      if (MASKED) p = (f == 0.f) ? 0.f : p;
-      lsum += p;
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(F[s][8 * hh + j], c2, -kb));
+      part[kc] += p;
       pk[kc][j] = (_Float16)p;
     }
   }
-  return lsum;
+  return (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // FP8 PV: the e4m3 codes of 448·p follow the running max itself (the schedule
 // the method fixes): p·448 = 2^((F - mx)·c + (m_tile - m) + log2 448), with
 // F - mx exact (both in [2^23, 2^24)); p·448 <= 448·2^(2^-20) < 464, so the
 // conversion cannot overflow.  P is packed as one 32-byte B operand.
-template <bool MASKED>
 __device__ __forceinline__ float exp_pack_fp8(const float (&F)[2][16], float mx, float c2, float cterm, v8i& pk) {
   float lsum = 0.f;
 #pragma unroll
@@ -259,11 +255,8 @@ __device__ __forceinline__ float exp_pack_fp8(const float (&F)[2][16], float mx,
     float p[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const float f = F[s][i0 + j];
-      float e = __builtin_amdgcn_exp2f(__builtin_fmaf(f - mx, c2, cterm));
-      if (MASKED) e = (f == 0.f) ? 0.f : e;
-      lsum += e;
-      p[j] = e;
+      p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[s][i0 + j] - mx, c2, cterm));
+      lsum += p[j];
     }
     int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
     pk[q] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
@@ -292,19 +285,49 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ vstage, int lan
   }
 }
 
-// Row sum of packed fp16 p: fp32 accumulation of the rounded values that PV
-// applies, two per instruction.
-__device__ __forceinline__ float sum_pk(const v8h (&pk)[4]) {
-  const v2h one = {(_Float16)1.0f, (_Float16)1.0f};
-  float s = 0.f;
+// Matrix phase with both parts (the steady state): PV of the previous tile and
+// QKᵀ of the current one in one scheduling region.  All K̂ fragment reads go
+// first; then every MFMA is followed by one V fragment read while any remain,
+// so each LDS read has several MFMAs (>= 256 cycles) to land before its use.
+template <int D, bool FP8>
+__device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, const char* __restrict__ vstage,
+                                            int lane, int r32, int gg, const v4i (&qf)[D / 32], v16i (&S)[2],
+                                            const v8h (&pk16)[4], const v8i& pk8, v16f (&O)[D / 32]) {
+  constexpr int DT = D / 32;
+  constexpr int NK = 2 * DT;                 // K̂ fragment reads (128-bit)
+  constexpr int NV = FP8 ? 2 * DT : 4 * DT;  // V fragment reads (128-bit)
+  constexpr int NQK = 2 * DT;                // QKᵀ MFMAs
+  constexpr int NPV = FP8 ? DT : 4 * DT;     // PV MFMAs
+  v4i kf[2][DT];
+  load_k_frags<D>(reinterpret_cast<const v4i*>(kstage), kf, r32, gg);
+  if (!FP8) {
+    const v8h* lv = reinterpret_cast<const v8h*>(vstage);
+    v8h vf[4 * DT];
 #pragma unroll
-  for (int kc = 0; kc < 4; ++kc)
+    for (int i = 0; i < 4 * DT; ++i) vf[i] = lv[i * 64 + lane];
+    qk_half<D>(kf, qf, S);
 #pragma unroll
-    for (int j = 0; j < 8; j += 2) {
-      const v2h pr = {pk[kc][j], pk[kc][j + 1]};
-      s = __builtin_amdgcn_fdot2(pr, one, s, false);
-    }
-  return s;
+    for (int kc = 0; kc < 4; ++kc)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[kc * DT + dt], pk16[kc], O[dt], 0, 0, 0);
+  } else {
+    const v8i* lv = reinterpret_cast<const v8i*>(vstage);
+    v8i vf[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vf[dt] = lv[dt * 64 + lane];
+    qk_half<D>(kf, qf, S);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[dt], pk8, O[dt], 0, 0, 0, 0, 0, 0);
+  }
+  // schedule: NK reads, then MFMA / read pairs, then the remaining MFMAs
+  __builtin_amdgcn_sched_group_barrier(0x100, NK, 0);
+#pragma unroll
+  for (int i = 0; i < NQK + NPV; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    if (i < NV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+  }
 }
 
 template <int D>
@@ -328,31 +351,61 @@ struct WaveCtx {
   float l_run;      // this lane's share of the row sum
 };
 
-// Softmax phase of one tile: scores -> P (kept for the next matrix phase), row
-// statistics and, when needed, the output rescale.  MASKED: keys past n or
-// (causal) after the row's query are excluded.
-template <int D, bool FP8, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2, int k0, int n, int qrow, int gg) {
+// Row max of the tile's scores (magic-biased; 0 when nothing is visible), over
+// both lanes of the row.
+__device__ __forceinline__ float row_max(const float (&F)[2][16]) {
+  float mx = 0.f;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) mx = max3f(mx, F[s][i], F[s][i + 1]);
+  return pair_max(mx);
+}
+
+// Softmax phase of one tile (masked entries already -inf): P for the next
+// matrix phase, the row statistics and, when the exponent reference moves,
+// the output rescale — O is rescaled in one place only.
+//
+// FP16: P is formed against the current reference m first.  If every lane's
+// sum of p stays <= 2^kLazyRescale, no p exceeds that bound and the tile is
+// done without a row max; otherwise (a row max passed m by more than
+// kLazyRescale, or the first visible tile of a row) m moves to the row max,
+// O and l are rescaled and P is formed again.  Softmax does not depend on the
+// reference and fp16 rounding is relative, so this changes nothing but
+// rounding.  FP8: the codes follow the running max exactly, tile by tile.
+template <int D, bool FP8>
+__device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2) {
   float F[2][16];
-  const float mx = scores<CAUSAL, MASKED>(c.S, F, k0, n, qrow, gg);
-  const float mt = tile_max(mx, c2);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // read the element by value first: a bit cast of an ext-vector element
+      // lvalue compiles to a read of element 0
+      const int bits = c.S[s][i];
+      F[s][i] = __int_as_float(bits);
+    }
   if (!FP8) {
-    // lazy reference: moves only when a row max passed it by more than kLazyRescale
-    if (__any(mt > c.m_run + kLazyRescale)) {
+    // a row that has seen no visible key keeps m = -inf: its p become +inf
+    // (visible) or 0 (masked), and the check below moves m
+    float lsum = exp_pack_fp16(F, c2, __builtin_fmaxf(c.m_run, -3.0e38f), c.pk16);
+    if (__any(!(lsum <= kLazyLimit))) {
+      const float mt = tile_max(row_max(F), c2);
       float m_new = __builtin_fmaxf(c.m_run, mt);
       m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
       rescale_o<D>(c.O, c.l_run, __builtin_amdgcn_exp2f(c.m_run - m_new));
       c.m_run = m_new;
+      lsum = exp_pack_fp16(F, c2, m_new, c.pk16);
     }
-    exp_pack_fp16<MASKED>(F, c2, c.m_run, c.pk16);
-    c.l_run += sum_pk(c.pk16);
+    c.l_run += lsum;
   } else {
+    const float mx = row_max(F);
+    const float mt = tile_max(mx, c2);
     float m_new = __builtin_fmaxf(c.m_run, mt);
     m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(c.m_run - m_new);
-    const float lsum = exp_pack_fp8<MASKED>(F, mx, c2, (mt - m_new) + kLog2E4M3Max, c.pk8);
-    if (__any(alpha != 1.f))
-      rescale_o<D>(c.O, c.l_run, alpha);
+    const float lsum = exp_pack_fp8(F, mx, c2, (mt - m_new) + kLog2E4M3Max, c.pk8);
+    if (__any(alpha != 1.f)) rescale_o<D>(c.O, c.l_run, alpha);
     c.m_run = m_new;
     c.l_run += lsum;
   }
@@ -413,6 +466,9 @@ void attn_fwd_kernel(AttnArgs a) {
   c.m_run = -__builtin_inff();
   c.l_run = 0.f;
 #pragma unroll
+  for (int kc = 0; kc < 4; ++kc) c.pk16[kc] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+  c.pk8 = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) c.O[dt][i] = 0.f;
@@ -434,29 +490,25 @@ void attn_fwd_kernel(AttnArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     const int k0 = t * kKBlock;
     const bool act = t < nact;
-    const bool have_p = t > 0 && t <= nact;  // P of tile t-1 is pending its PV
     // ---- matrix phase: PV of tile t-1, QKᵀ of tile t
-    __builtin_amdgcn_s_setprio(1);
     if (lead && t + 2 < ntiles)
       issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, t + 2, smem + ((t + 2) % kRingStages) * G::STAGE, w, lane);
-    if (have_p)
-      pv_tile<D, FP8>(smem + ((t + kRingStages - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, c.pk16, c.pk8,
-                      c.O);
-    if (act) {
-      v4i kf[2][DT];
-      load_k_frags<D>(reinterpret_cast<const v4i*>(smem + (t % kRingStages) * G::STAGE), kf, r32, gg);
-      qk_half<D>(kf, c.qf, c.S);
-    }
-    __builtin_amdgcn_s_setprio(0);
+    // One place for both MFMA parts keeps O and S in fixed registers.  At t = 0
+    // the pending P is zero (O += 0·V of tile 0, which has landed); at t = nact
+    // the QKᵀ result is not used.
+    if (t <= nact && nact > 0)
+      matrix_both<D, FP8>(smem + (t % kRingStages) * G::STAGE,
+                          smem + ((t == 0 ? 0 : t - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, r32, gg, c.qf,
+                          c.S, c.pk16, c.pk8, c.O);
     barrier_only();
     // ---- softmax phase: tile t
     if (act) {
-      const float c2 = dq * load_uniform(ksc, t) * kLog2e;
+      // c > 0 keeps -inf·c = -inf for masked keys; a zero scale means all
+      // scores of the tile are 0, for which the smallest normal gives the same
+      const float c2 = __builtin_fmaxf(dq * load_uniform(ksc, t) * kLog2e, 1.17549435e-38f);
       const bool full = (k0 + kKBlock <= n) && (!CAUSAL || k0 + kKBlock - 1 <= wq_lo);
-      if (full)
-        softmax_phase<D, FP8, CAUSAL, false>(c, c2, k0, n, qrow, gg);
-      else
-        softmax_phase<D, FP8, CAUSAL, true>(c, c2, k0, n, qrow, gg);
+      if (!full) mask_scores<CAUSAL>(c.S, k0, n, qrow, gg);
+      softmax_phase<D, FP8>(c, c2);
     }
     if (lead) {
       // tile t+1 landed before anyone's next matrix phase (tile t+2 may still fly)
