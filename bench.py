@@ -122,6 +122,88 @@ def cpu_baseline(w, x, budget_s=15.0):
                       f"of attention; {t_total:.1f} s of CPU time"}
 
 
+# ---------------------------------------------------------------------------
+# rocprofv3 result databases (rocpd SQLite): per-kernel summaries and the HBM
+# traffic of the attention kernel.
+
+def _rocpd_rows(db, sql):
+    import sqlite3
+    con = sqlite3.connect(db)
+    try:
+        return con.execute(sql).fetchall()
+    finally:
+        con.close()
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def rocprof_counters(db):
+    """{kernel: {counter: mean value per dispatch}} (values of one dispatch summed over instances)."""
+    per = {}
+    for disp, kname, cname, val in _rocpd_rows(
+            db, "select dispatch_id, kernel_name, counter_name, value from counters_collection"):
+        key = (disp, _short(kname), cname)
+        per[key] = per.get(key, 0.0) + float(val)
+    agg = {}
+    for (disp, k, cname), v in per.items():
+        agg.setdefault(k, {}).setdefault(cname, []).append(v)
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in agg.items()}
+
+
+def rocprof_summary(db):
+    lines = [f"# {os.path.basename(db)}"]
+    try:
+        rows = _rocpd_rows(db, "select name, count(*), avg(duration), sum(duration) from kernels group by name "
+                               "order by sum(duration) desc")
+    except Exception:
+        rows = []
+    if rows:
+        total = sum(r[3] for r in rows)
+        lines.append("kernel | calls | avg us | share")
+        for name, calls, avg, tot in rows:
+            lines.append(f"{_short(name)} | {calls} | {avg / 1e3:.2f} | {100 * tot / total:.1f}%")
+    try:
+        ctr = rocprof_counters(db)
+    except Exception:
+        ctr = {}
+    for k, cs in ctr.items():
+        lines.append(f"{k}: " + ", ".join(f"{c}={v:.6g}" for c, v in sorted(cs.items())))
+    return "\n".join(lines)
+
+
+def _copy_factor(db, counter, nbytes=1 << 30):
+    """Bytes per counter unit, from the plain copy kernel of --copy-calibration 1024."""
+    ctr = rocprof_counters(db)
+    vals = [cs[counter] for k, cs in ctr.items() if "copyBuffer" in k and counter in cs]
+    if not vals:
+        raise SystemExit(f"no copy kernel with {counter} in {db}")
+    return nbytes / vals[0]
+
+
+def write_traffic(workload, fetch_db, write_db, cal_fetch_db, cal_write_db):
+    ff, wf = _copy_factor(cal_fetch_db, "FETCH_SIZE"), _copy_factor(cal_write_db, "WRITE_SIZE")
+    fetch = [cs["FETCH_SIZE"] for k, cs in rocprof_counters(fetch_db).items() if k.startswith("sage::attn_fwd_kernel")]
+    write = [cs["WRITE_SIZE"] for k, cs in rocprof_counters(write_db).items() if k.startswith("sage::attn_fwd_kernel")]
+    if not fetch or not write:
+        raise SystemExit("no attention kernel dispatches in the counter databases")
+    rec = {"fetch_bytes": round(fetch[0] * ff), "write_bytes": round(write[0] * wf),
+           "fetch_factor_bytes_per_unit": ff, "write_factor_bytes_per_unit": wf,
+           "source_digest": source_digest()}
+    rec["bytes_per_launch"] = rec["fetch_bytes"] + rec["write_bytes"]
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            allrec = json.load(fh)
+    except (OSError, ValueError):
+        allrec = {}
+    allrec[workload] = rec
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(allrec, fh, indent=1, sort_keys=True)
+    print(json.dumps({workload: rec}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,10 +213,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates the HBM byte counters)")
+    ap.add_argument("--rocprof-summary", nargs="+", metavar="DB",
+                    help="only summarise rocprofv3 result databases (kernel durations, counters per dispatch)")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_DB", "WRITE_DB", "CAL_FETCH_DB", "CAL_WRITE_DB"),
+                    help="with --workload: store the attention kernel's HBM bytes per launch, scaled by the "
+                         "copy calibration (--copy-calibration 1024 runs), in profiles/attn_traffic.json")
     args = ap.parse_args()
+    if args.rocprof_summary:
+        for db in args.rocprof_summary:
+            print(rocprof_summary(db))
+        return
+    if args.write_traffic:
+        write_traffic(args.workload, *args.write_traffic)
+        return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested); "
-              "the forward shards by heads/sequences with no collective, see the design notes", file=sys.stderr)
+        print(f"bench.py: measures one GPU only (--gpus {args.gpus} requested); the forward shards by "
+              "(batch, head) or by sequence with no collective, so N GPUs run N independent shards", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -412,14 +412,27 @@ __device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2) {
 }
 
 // Workgroup: 8 waves x 32 queries = 256 queries (two Q scale blocks), two waves
-// per SIMD.  Waves 0-3 (group A) and 4-7 (group B) run the same pipeline one
-// phase apart — matrix phase (PV of tile t-1, QKᵀ of tile t) then softmax
-// phase (tile t), a workgroup barrier between phases — so on every SIMD one
+// per SIMD (waves w and w+4 share one).  Waves 0-3 (group A) and 4-7 (group B)
+// run the same per-tile work in opposite orders, so that on every SIMD one
 // wave's MFMAs overlap the other wave's softmax.  Group A streams the tiles.
 constexpr int kAttnWaves = 8;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kAttnRows = 32 * kAttnWaves;
-constexpr int kRingStages = 4;  // tile t+2 loads while group B may still read tile t-1
+constexpr int kAhead = 2;                // tiles requested ahead of the one being read
+constexpr int kRingStages = kAhead + 2;  // + tile t (group A) and tile t-1 (group B's PV)
+static_assert(kAhead >= 1 && kAhead <= 3, "wait_tiles handles up to two tiles in flight");
+
+// Wait until at most `pending` tiles (L DMA instructions each) of this wave
+// are still in flight.
+template <int L>
+__device__ __forceinline__ void wait_tiles(int pending) {
+  if (pending >= 2)
+    wait_dma<2 * L>();
+  else if (pending == 1)
+    wait_dma<L>();
+  else
+    wait_dma<0>();
+}
 
 template <int D, bool FP8, bool CAUSAL>
 __global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads), amdgpu_waves_per_eu(2, 2)))
@@ -474,25 +487,35 @@ void attn_fwd_kernel(AttnArgs a) {
     for (int i = 0; i < 16; ++i) c.O[dt][i] = 0.f;
 
   if (lead) {
-    issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, 0, smem, w, lane);
-    if (ntiles > 1) {
-      issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, 1, smem + G::STAGE, w, lane);
-      wait_dma<L>();  // tile 0 landed
-    } else {
-      wait_dma<0>();
-    }
+    const int first = min(kAhead, ntiles);
+    for (int t = 0; t < first; ++t)
+      issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, t, smem + t * G::STAGE, w, lane);
+    wait_tiles<L>(first - 1);  // tile 0 landed
   }
   barrier_only();
-  if (!lead) barrier_only();  // group B runs one phase behind
 
   // tiles this wave takes part in: 0..nact-1 (causal: keys up to its last query)
   const int nact = !wave_rows ? 0 : CAUSAL ? min(ntiles, wq_hi / kKBlock + 1) : ntiles;
+  auto softmax_step = [&](int u) {
+    if (u < nact) {
+      const int k0 = u * kKBlock;
+      // c > 0 keeps -inf·c = -inf for masked keys; a zero scale means all
+      // scores of the tile are 0, for which the smallest normal gives the same
+      const float c2 = __builtin_fmaxf(dq * load_uniform(ksc, u) * kLog2e, 1.17549435e-38f);
+      const bool full = (k0 + kKBlock <= n) && (!CAUSAL || k0 + kKBlock - 1 <= wq_lo);
+      if (!full) mask_scores<CAUSAL>(c.S, k0, n, qrow, gg);
+      softmax_phase<D, FP8>(c, c2);
+    }
+  };
+  // One workgroup barrier per tile.  Group A runs matrix(t) then softmax(t),
+  // group B softmax(t-1) then matrix(t), so on each SIMD one wave's MFMAs
+  // overlap the other wave's exponentials; matrix(t) = PV of tile t-1 and QKᵀ
+  // of tile t.
   for (int t = 0; t < ntiles; ++t) {
-    const int k0 = t * kKBlock;
-    const bool act = t < nact;
-    // ---- matrix phase: PV of tile t-1, QKᵀ of tile t
-    if (lead && t + 2 < ntiles)
-      issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, t + 2, smem + ((t + 2) % kRingStages) * G::STAGE, w, lane);
+    if (lead && t + kAhead < ntiles)
+      issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, t + kAhead,
+                         smem + ((t + kAhead) % kRingStages) * G::STAGE, w, lane);
+    if (!lead && t > 0) softmax_step(t - 1);
     // One place for both MFMA parts keeps O and S in fixed registers.  At t = 0
     // the pending P is zero (O += 0·V of tile 0, which has landed); at t = nact
     // the QKᵀ result is not used.
@@ -500,28 +523,14 @@ void attn_fwd_kernel(AttnArgs a) {
       matrix_both<D, FP8>(smem + (t % kRingStages) * G::STAGE,
                           smem + ((t == 0 ? 0 : t - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, r32, gg, c.qf,
                           c.S, c.pk16, c.pk8, c.O);
-    barrier_only();
-    // ---- softmax phase: tile t
-    if (act) {
-      // c > 0 keeps -inf·c = -inf for masked keys; a zero scale means all
-      // scores of the tile are 0, for which the smallest normal gives the same
-      const float c2 = __builtin_fmaxf(dq * load_uniform(ksc, t) * kLog2e, 1.17549435e-38f);
-      const bool full = (k0 + kKBlock <= n) && (!CAUSAL || k0 + kKBlock - 1 <= wq_lo);
-      if (!full) mask_scores<CAUSAL>(c.S, k0, n, qrow, gg);
-      softmax_phase<D, FP8>(c, c2);
-    }
-    if (lead) {
-      // tile t+1 landed before anyone's next matrix phase (tile t+2 may still fly)
-      if (t + 2 < ntiles)
-        wait_dma<L>();
-      else
-        wait_dma<0>();
-    }
+    if (lead) softmax_step(t);
+    // tile t+1 landed before anyone's next matrix phase (later tiles may fly)
+    if (lead) wait_tiles<L>(max(0, min(kAhead - 1, ntiles - 2 - t)));
     barrier_only();
   }
+  if (!lead && ntiles > 0) softmax_step(ntiles - 1);
   if (nact == ntiles && ntiles > 0)
     pv_tile<D, FP8>(smem + ((ntiles - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, c.pk16, c.pk8, c.O);
-  if (lead) barrier_only();  // matches group B's extra barrier
 
   // Epilogue: o = O / l (FP16) or O·δV / l with l holding 448·Σp (FP8).
   const float l_tot = pair_sum(c.l_run);
