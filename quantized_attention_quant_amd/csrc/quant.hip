@@ -39,19 +39,22 @@ __global__ __launch_bounds__(kThreads) void k_colsum_kernel(const uint16_t* __re
   if (t0 >= n) return;
   const int t1 = min(n, t0 + kColsumChunk);
   const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
-  int64_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // fp64 partial sums are exact: every fp16 value is a multiple of 2^-24 below
+  // 2^16 in magnitude, and a thread adds at most kColsumChunk / RPP of them
+  double acc[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
   for (int t = t0 + rr; t < t1; t += RPP) {
     const v4i raw = *reinterpret_cast<const v4i*>(k + (row0 + t) * D + cg * 8);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t w = (uint32_t)raw[j];
-      acc[2 * j] += fp16_fixed24((uint16_t)(w & 0xffffu));
-      acc[2 * j + 1] += fp16_fixed24((uint16_t)(w >> 16));
+      acc[2 * j] += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+      acc[2 * j + 1] += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
     }
   }
+  static_assert(kColsumChunk / RPP <= 8192, "fp64 partial sums must stay exact");
   __shared__ int64_t red[RPP][D];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[rr][cg * 8 + j] = acc[j];
+  for (int j = 0; j < 8; ++j) red[rr][cg * 8 + j] = (int64_t)(acc[j] * 0x1p24);  // integral, < 2^53
   __syncthreads();
   if (threadIdx.x < D) {
     int64_t s = 0;
@@ -73,12 +76,20 @@ __device__ __forceinline__ float block_max256(float v) {
   return r;
 }
 
-// Symmetric INT8 code of x with block scale s (s == 0 -> 0): IEEE fp32 divide,
-// round half to even, clamp to ±127.
-__device__ __forceinline__ int int8_code(float x, float s) {
-  if (!(s > 0.f)) return 0;
-  const float r = __builtin_rintf(x / s);
-  return (int)fminf(fmaxf(r, -kInt8Max), kInt8Max);
+// Symmetric INT8 code of x for a block scale s > 0: rint of the IEEE fp32
+// quotient fl32(x/s), clamped to ±127.  The quotient is first formed as
+// y = fl32(x·r) with r = fl32(1/s): since |x/s| <= 127·(1 + 2^-23), y lies
+// within 2.3e-5 of fl32(x/s), so rint(y) is the same integer unless y is within
+// that distance of a half-integer; only then is the exact quotient divided out.
+constexpr float kTieGuard = 6.103515625e-05f;  // 2^-14 > 2.3e-5
+
+__device__ __attribute__((noinline)) float exact_code(float x, float s) { return __builtin_rintf(x / s); }
+
+__device__ __forceinline__ int int8_code(float x, float s, float r) {
+  const float y = x * r;
+  float c = __builtin_rintf(y);
+  if (__builtin_expect(__builtin_fabsf(__builtin_fabsf(y - c) - 0.5f) <= kTieGuard, 0)) c = exact_code(x, s);
+  return (int)__builtin_amdgcn_fmed3f(c, -kInt8Max, kInt8Max);
 }
 
 __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
@@ -110,14 +121,16 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* _
 #pragma unroll
   for (int j = 0; j < 8; ++j) shift[j] = 0.f;
   if (SMOOTH) {
-    // km = fp32(exact sum * 2^-24 / n): one fp64 divide, one rounding.
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      shift[j] = (float)((double)colsum[hs * D + cg * 8 + j] * 0x1p-24 / (double)n);
-    if (blk == 0 && rr == 0) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kmean[hs * D + cg * 8 + j] = shift[j];
+    // km = fp32(exact sum * 2^-24 / n): one fp64 divide per channel, one rounding
+    __shared__ float km_s[D];
+    if (threadIdx.x < D) {
+      const float km = (float)((double)colsum[hs * D + threadIdx.x] * 0x1p-24 / (double)n);
+      km_s[threadIdx.x] = km;
+      if (blk == 0) kmean[hs * D + threadIdx.x] = km;
     }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) shift[j] = km_s[cg * 8 + j];
   }
   float x[PASSES][8];
   float amax = 0.f;
@@ -143,13 +156,18 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* _
   }
   amax = block_max256(amax);
   const float s = amax / kInt8Max;
+  const float r = 1.0f / s;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int t = t0 + rr + p * RPP;
     if (t < n) {
-      uint2 w;
-      w.x = pack4_i8(int8_code(x[p][0], s), int8_code(x[p][1], s), int8_code(x[p][2], s), int8_code(x[p][3], s));
-      w.y = pack4_i8(int8_code(x[p][4], s), int8_code(x[p][5], s), int8_code(x[p][6], s), int8_code(x[p][7], s));
+      uint2 w = {0u, 0u};  // an all-zero block (s = 0) has all codes 0
+      if (s > 0.f) {
+        w.x = pack4_i8(int8_code(x[p][0], s, r), int8_code(x[p][1], s, r), int8_code(x[p][2], s, r),
+                       int8_code(x[p][3], s, r));
+        w.y = pack4_i8(int8_code(x[p][4], s, r), int8_code(x[p][5], s, r), int8_code(x[p][6], s, r),
+                       int8_code(x[p][7], s, r));
+      }
       *reinterpret_cast<uint2*>(codes + (row0 + t) * D + cg * 8) = w;
     }
   }

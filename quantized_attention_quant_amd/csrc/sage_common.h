@@ -74,14 +74,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * q + (x < r ? x : r) + local;
 }
 
-// fp16 bits -> exact integer value * 2^24 (every fp16 is a multiple of 2^-24).
-__device__ __forceinline__ int64_t fp16_fixed24(uint16_t hbits) {
-  const int e = (hbits >> 10) & 31;
-  const int m = hbits & 1023;
-  const int64_t mag = e == 0 ? (int64_t)m : ((int64_t)(1024 + m) << (e - 1));
-  return (hbits & 0x8000) ? -mag : mag;
-}
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -116,6 +116,35 @@ def test_quant_qk_bit_exact_small(n, d):
     assert (got2.view(np.uint32) == ref2.view(np.uint32)).all()
 
 
+def test_quant_rounding_boundaries():
+    """Quotients at and next to half-integers: the kernel's reciprocal path must
+    hand these to the exact fp32 division and round ties to even, exactly as the
+    oracle does."""
+    say("case quant rounding boundaries")
+    rng = np.random.default_rng(5)
+    n, d = 256, 64
+    half = np.arange(-126, 126) + 0.5                      # exact ties (delta = 1)
+    near = np.concatenate([half + 2.0 ** -9, half - 2.0 ** -9, half + 2.0 ** -6])
+    vals = np.concatenate([half, near, rng.uniform(-127, 127, 4096)])
+    q = rng.choice(vals, size=(1, 2, n, d)).astype(np.float16)
+    q[..., 0, 0] = 127.0                                   # every block attains 127 -> delta = 1
+    q[..., 128, 0] = -127.0
+    # K: token pairs of opposite sign give an exactly zero column mean, so the
+    # smoothed values are the fp16 inputs themselves
+    kh = rng.choice(vals, size=(1, 2, n // 2, d)).astype(np.float16)
+    kh[..., ::32, 1] = 127.0                               # every 64-token block attains 127
+    k = np.empty((1, 2, n, d), np.float16)
+    k[..., 0::2, :] = kh
+    k[..., 1::2, :] = -kh
+    got = {k2: host(v2) for k2, v2 in sage.sage_quant_qk(dev(q), dev(k)).items()}
+    ref = O.quant_qk_dense(q, k)
+    assert (ref["k_mean"] == 0).all()
+    ties = np.abs(np.abs(q.astype(np.float64)) % 1.0 - 0.5) == 0
+    assert ties.sum() > 1000
+    for key in ("q_int8", "k_int8", "q_scale", "k_scale", "k_mean"):
+        assert (got[key].view(np.uint8) == ref[key].view(np.uint8)).all(), key
+
+
 def test_quant_zero_blocks_and_constant_k():
     say("case quant zero blocks")
     q = np.zeros((1, 1, 300, 64), np.float16)
