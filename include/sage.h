@@ -115,34 +115,47 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
 
 /* ------------------------------------------------------------------------
  * sage_attn_fwd — full forward on dense [B,H,N,d] fp16 tensors.
- *   q, k, v inputs; o output fp16 [B,H,N,d] (may not alias the inputs).
+ *   q fp16 [B,H,N,d]; k, v fp16 [B,H_kv,N,d]; o output fp16 [B,H,N,d] (may not
+ *   alias the inputs).  H_kv divides H: query head h attends with K/V head
+ *   h / (H / H_kv) (grouped-query or multi-query attention; H_kv = H is plain
+ *   multi-head attention, and K smoothing and K blocks are per K/V head).
+ *   lse: NULL, or fp32 [B,H,N] receiving, per query row, the natural-log sum
+ *   of exp of the row's scaled scores s = δQ·δK·(q̂·k̂) over the visible keys
+ *   (smoothed K: exact attention shifted by the row constant q·km·sm_scale),
+ *   for merging partial results over key ranges; 4-byte aligned, no overlap.
  *   is_causal != 0 masks key j > query i (deepseek.csdn.net post: is_causal).
  *   pv_mode selects FP16 PV or FP8-e4m3 PV.  sm_scale <= 0 -> 1/sqrt(d).
  *   The pre-pass (smoothing, quantisation, V packing) writes into the
  *   caller's workspace of at least sage_attn_workspace_size(...) bytes; its
  *   layout is internal (see sage_test_workspace_layout).
+ *   Errors: SAGE_ERR_INVALID_ARGUMENT for null or misaligned (16-byte) tensor
+ *   pointers, a workspace not 256-byte aligned, overlapping outputs, H_kv not
+ *   dividing H, d not in {64, 128}, N > 2^23, B or H > 65535, or a NaN/Inf
+ *   sm_scale; SAGE_ERR_WORKSPACE_TOO_SMALL; SAGE_ERR_DEVICE if a launch fails.
+ *   Nothing is launched on error.  Asynchronous on `stream`.
  */
-size_t sage_attn_workspace_size(int B, int H, int N, int d, sage_pv_mode_t pv_mode);
-sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H,
-                            int N, int d, sage_layout_t layout, int is_causal,
-                            sage_pv_mode_t pv_mode, float sm_scale, void* workspace,
-                            size_t workspace_bytes, sage_stream_t stream);
+size_t sage_attn_workspace_size(int B, int H, int H_kv, int N, int d, sage_pv_mode_t pv_mode);
+sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                            int B, int H, int H_kv, int N, int d, sage_layout_t layout,
+                            int is_causal, sage_pv_mode_t pv_mode, float sm_scale,
+                            void* workspace, size_t workspace_bytes, sage_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * sage_attn_varlen_fwd — forward on packed variable-length sequences.
  *   (jsqmd "SageAttention完全指南", API list: sageattn_varlen)
- *   q, k, v, o packed fp16 [H,T,d]; cu_seqlens device int32 [nseq+1] with
- *   cu[0]=0, non-decreasing, cu[nseq]=total_tokens, every length <=
- *   max_seqlen.  Means, quantisation blocks and the causal mask are per
- *   sequence.  Empty sequences are allowed.
+ *   q, o packed fp16 [H,T,d]; k, v packed fp16 [H_kv,T,d] (H_kv divides H, as
+ *   for sage_attn_fwd); lse NULL or fp32 [H,T].  cu_seqlens device int32
+ *   [nseq+1] with cu[0]=0, non-decreasing, cu[nseq]=total_tokens, every
+ *   length <= max_seqlen.  Means, quantisation blocks and the causal mask are
+ *   per sequence.  Empty sequences are allowed.
  */
-size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H, int d,
-                                       sage_pv_mode_t pv_mode);
+size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H,
+                                       int H_kv, int d, sage_pv_mode_t pv_mode);
 sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o,
-                                   const int32_t* cu_seqlens, int nseq, int max_seqlen,
-                                   int64_t total_tokens, int H, int d, int is_causal,
-                                   sage_pv_mode_t pv_mode, float sm_scale, void* workspace,
-                                   size_t workspace_bytes, sage_stream_t stream);
+                                   float* lse, const int32_t* cu_seqlens, int nseq,
+                                   int max_seqlen, int64_t total_tokens, int H, int H_kv, int d,
+                                   int is_causal, sage_pv_mode_t pv_mode, float sm_scale,
+                                   void* workspace, size_t workspace_bytes, sage_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * Test hooks (stable; prefix sage_test_).
@@ -152,9 +165,10 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  *   [0] q_int8, [1] k_int8, [2] q_scale, [3] k_scale, [4] k_mean,
  *   [5] packed V, [6] v_scale (fp8 mode; an empty region in fp16 mode),
  *   [7] total size (internal scratch sits between [6] and [7]).
- *   For dense calls pass B,H,N,d (nseq,total_tokens ignored); for varlen pass
+ *   For dense calls pass B,H,H_kv,N,d (total_tokens ignored); for varlen pass
  *   B = nseq, N = max_seqlen and total_tokens.  offsets_out is HOST memory.
- *   The int8/scale/mean regions use the same layouts as sage_quant_qk.
+ *   The int8/scale/mean regions use the same layouts as sage_quant_qk, with
+ *   H_kv heads for K.
  *
  * sage_test_qk_tiles: int32 tiles of Q̂K̂ᵀ (128 queries x 64 keys each, row =
  *   query) for a list of (b, h, q_block, k_block) quadruples (device int32
@@ -164,16 +178,18 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  */
 /*
  * sage_test_attn_from_workspace: launch only the fused attention kernel on a
- *   workspace that a preceding sage_attn_fwd call with the same B,H,N,d,
+ *   workspace that a preceding sage_attn_fwd call with the same B,H,H_kv,N,d,
  *   is_causal and pv_mode has filled (its pre-pass results are reused as they
- *   are); writes o fp16 [B,H,N,d].  Used to time the attention kernel alone.
- *   Same validation as sage_attn_fwd.
+ *   are); writes o fp16 [B,H,N,d] (no LSE).  Used to time the attention
+ *   kernel alone.  Same validation as sage_attn_fwd.
  */
-sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int N, int d, int is_causal,
-                                            sage_pv_mode_t pv_mode, const void* workspace,
-                                            size_t workspace_bytes, sage_stream_t stream);
-sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int N, int64_t total_tokens,
-                                         int d, sage_pv_mode_t pv_mode, size_t offsets_out[8]);
+sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int N, int d,
+                                            int is_causal, sage_pv_mode_t pv_mode,
+                                            const void* workspace, size_t workspace_bytes,
+                                            sage_stream_t stream);
+sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int N,
+                                         int64_t total_tokens, int d, sage_pv_mode_t pv_mode,
+                                         size_t offsets_out[8]);
 sage_status_t sage_test_qk_tiles(const int8_t* q_int8, const int8_t* k_int8, int B, int H, int N,
                                  int d, const int32_t* tile_list, int n_tiles, int32_t* out,
                                  sage_stream_t stream);

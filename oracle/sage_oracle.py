@@ -363,6 +363,27 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
     return out.astype(np.float16)
 
 
+def score_lse_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndarray, k_scale: np.ndarray,
+                   rows: Sequence[int], causal: bool) -> np.ndarray:
+    """Natural-log sum of exp of each row's dequantised scores over its visible
+    keys, the quantity that merges partial softmax results over key ranges
+    ([IP] §3.1 online softmax keeps it as (m, l): lse = m + log l):
+
+        lse_i = log Σ_{j visible} exp(δQ_i · δK_j · (q̂_i · k̂_j)).
+
+    Plain definition in fp64 (shifted by the row max before exp).  Returns
+    fp64 [len(rows)]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    n = k_int8.shape[0]
+    keys = np.arange(n)
+    acc = q_int8[rows].astype(np.float64) @ k_int8.astype(np.float64).T
+    s = acc * q_scale[rows // Q_BLOCK].astype(np.float64)[:, None] * k_scale[keys // K_BLOCK].astype(np.float64)[None, :]
+    if causal:
+        s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+    mx = s.max(axis=1)
+    return mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+
+
 # ----------------------------------------------------------------------------
 # Plain definition: fp64 scaled-dot-product attention ([IP] §2.1)
 # ----------------------------------------------------------------------------

@@ -39,18 +39,18 @@ SIGNATURES = {
                                  _c.c_float, _P, _P, _P, _P, _P, _P, _c.c_size_t, _P]),
     "sage_quant_v_fp8": (_c.c_int, [_P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P, _c.c_int64,
                                     _P, _P, _P]),
-    "sage_attn_workspace_size": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
-    "sage_attn_fwd": (_c.c_int, [_P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
-                                 _c.c_int, _c.c_float, _P, _c.c_size_t, _P]),
+    "sage_attn_workspace_size": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int]),
+    "sage_attn_fwd": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                 _c.c_int, _c.c_int, _c.c_float, _P, _c.c_size_t, _P]),
     "sage_attn_varlen_workspace_size": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int64, _c.c_int, _c.c_int,
-                                                      _c.c_int]),
-    "sage_attn_varlen_fwd": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int64, _c.c_int, _c.c_int,
-                                        _c.c_int, _c.c_int, _c.c_float, _P, _c.c_size_t, _P]),
-    "sage_test_workspace_layout": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64, _c.c_int,
-                                              _c.c_int, _c.POINTER(_c.c_size_t)]),
+                                                      _c.c_int, _c.c_int]),
+    "sage_attn_varlen_fwd": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int64, _c.c_int,
+                                        _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _P, _c.c_size_t, _P]),
+    "sage_test_workspace_layout": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64,
+                                              _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t)]),
     "sage_test_qk_tiles": (_c.c_int, [_P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P, _c.c_int, _P, _P]),
     "sage_test_attn_from_workspace": (_c.c_int, [_P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
-                                                 _P, _c.c_size_t, _P]),
+                                                 _c.c_int, _P, _c.c_size_t, _P]),
 }
 
 
@@ -185,62 +185,82 @@ def sage_quant_v_fp8(v: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
     return codes, scale
 
 
-def sage_attn_workspace_size(B: int, H: int, N: int, d: int, pv_mode: str = "fp16") -> int:
-    return int(lib().sage_attn_workspace_size(B, H, N, d, PV_MODES[pv_mode]))
+def sage_attn_workspace_size(B: int, H: int, N: int, d: int, pv_mode: str = "fp16",
+                             H_kv: Optional[int] = None) -> int:
+    return int(lib().sage_attn_workspace_size(B, H, H if H_kv is None else H_kv, N, d, PV_MODES[pv_mode]))
+
+
+def _lse_out(return_lse: bool, lse: Optional[torch.Tensor], shape, device) -> Optional[torch.Tensor]:
+    if lse is not None:
+        _need(lse, "lse", torch.float32, len(shape))
+        if tuple(lse.shape) != tuple(shape):
+            raise ValueError(f"lse must have shape {tuple(shape)}")
+        return lse
+    return torch.empty(shape, dtype=torch.float32, device=device) if return_lse else None
 
 
 def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
                   pv_mode: str = "fp16", sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
-                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Dense fp16 [B,H,N,d] forward; returns o fp16 [B,H,N,d]."""
+                  workspace: Optional[torch.Tensor] = None, stream=None, return_lse: bool = False,
+                  lse: Optional[torch.Tensor] = None):
+    """Dense forward: q fp16 [B,H,N,d], k and v fp16 [B,H_kv,N,d] (H_kv divides H).
+    Returns o fp16 [B,H,N,d], or (o, lse fp32 [B,H,N]) when return_lse or lse is given."""
     L = lib()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, torch.float16, 4)
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError("q, k, v shapes differ")
     B, H, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError("k and v must be [B,H_kv,N,d] with q's B, N and d")
+    H_kv = k.shape[1]
     if pv_mode not in PV_MODES:
         raise ValueError(f"pv_mode must be one of {list(PV_MODES)}")
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.float16, 4)
-    ws = _alloc_ws(sage_attn_workspace_size(B, H, N, d, pv_mode), q.device, workspace)
-    st = L.sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, N, d, LAYOUT_HND,
-                         int(bool(is_causal)), PV_MODES[pv_mode], float(sm_scale), ws.data_ptr(),
+    lse_t = _lse_out(return_lse, lse, (B, H, N), q.device)
+    ws = _alloc_ws(sage_attn_workspace_size(B, H, N, d, pv_mode, H_kv), q.device, workspace)
+    st = L.sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse_t), B, H, H_kv, N, d,
+                         LAYOUT_HND, int(bool(is_causal)), PV_MODES[pv_mode], float(sm_scale), ws.data_ptr(),
                          ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sage_attn_fwd")
-    return o
+    return o if lse_t is None else (o, lse_t)
 
 
 def sage_attn_varlen_workspace_size(nseq: int, max_seqlen: int, total_tokens: int, H: int, d: int,
-                                    pv_mode: str = "fp16") -> int:
-    return int(lib().sage_attn_varlen_workspace_size(nseq, max_seqlen, total_tokens, H, d, PV_MODES[pv_mode]))
+                                    pv_mode: str = "fp16", H_kv: Optional[int] = None) -> int:
+    return int(lib().sage_attn_varlen_workspace_size(nseq, max_seqlen, total_tokens, H, H if H_kv is None else H_kv,
+                                                     d, PV_MODES[pv_mode]))
 
 
 def sage_attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                          max_seqlen: int, is_causal: bool = False, pv_mode: str = "fp16", sm_scale: float = 0.0,
                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                         stream=None) -> torch.Tensor:
-    """Packed fp16 [H,T,d] forward with int32 cu_seqlens [nseq+1] (device)."""
+                         stream=None, return_lse: bool = False, lse: Optional[torch.Tensor] = None):
+    """Packed forward: q fp16 [H,T,d], k and v fp16 [H_kv,T,d], int32 cu_seqlens [nseq+1]
+    (device).  Returns o fp16 [H,T,d], or (o, lse fp32 [H,T])."""
     L = lib()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, torch.float16, 3)
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError("q, k, v shapes differ")
     nseq, N, T, H, d = _varlen_dims(q, cu_seqlens, max_seqlen)
+    if k.shape != v.shape or k.shape[1:] != q.shape[1:]:
+        raise ValueError("k and v must be [H_kv,T,d] with q's T and d")
+    H_kv = k.shape[0]
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.float16, 3)
-    ws = _alloc_ws(sage_attn_varlen_workspace_size(nseq, N, T, H, d, pv_mode), q.device, workspace)
-    st = L.sage_attn_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cu_seqlens.data_ptr(),
-                                nseq, N, T, H, d, int(bool(is_causal)), PV_MODES[pv_mode], float(sm_scale),
-                                ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    lse_t = _lse_out(return_lse, lse, (H, T), q.device)
+    ws = _alloc_ws(sage_attn_varlen_workspace_size(nseq, N, T, H, d, pv_mode, H_kv), q.device, workspace)
+    st = L.sage_attn_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse_t),
+                                cu_seqlens.data_ptr(), nseq, N, T, H, H_kv, d, int(bool(is_causal)),
+                                PV_MODES[pv_mode], float(sm_scale), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                _stream(stream))
     _check(st, "sage_attn_varlen_fwd")
-    return o
+    return o if lse_t is None else (o, lse_t)
 
 
 def sage_test_workspace_layout(varlen: bool, B: int, H: int, N: int, total_tokens: int, d: int,
-                               pv_mode: str = "fp16") -> Sequence[int]:
+                               pv_mode: str = "fp16", H_kv: Optional[int] = None) -> Sequence[int]:
     arr = (ctypes.c_size_t * 8)()
-    st = lib().sage_test_workspace_layout(int(bool(varlen)), B, H, N, total_tokens, d, PV_MODES[pv_mode], arr)
+    st = lib().sage_test_workspace_layout(int(bool(varlen)), B, H, H if H_kv is None else H_kv, N, total_tokens, d,
+                                          PV_MODES[pv_mode], arr)
     _check(st, "sage_test_workspace_layout")
     return list(arr)
 
@@ -261,12 +281,13 @@ def sage_test_qk_tiles(q_int8: torch.Tensor, k_int8: torch.Tensor, tile_list: to
 
 
 def sage_test_attn_from_workspace(out: torch.Tensor, workspace: torch.Tensor, is_causal: bool = False,
-                                  pv_mode: str = "fp16", stream=None) -> torch.Tensor:
+                                  pv_mode: str = "fp16", stream=None, H_kv: Optional[int] = None) -> torch.Tensor:
     """Run only the fused attention kernel on a workspace filled by sage_attn_fwd
     (same shapes and options); out fp16 [B,H,N,d] is written and returned."""
     _need(out, "out", torch.float16, 4)
     B, H, N, d = out.shape
-    st = lib().sage_test_attn_from_workspace(out.data_ptr(), B, H, N, d, int(bool(is_causal)), PV_MODES[pv_mode],
+    st = lib().sage_test_attn_from_workspace(out.data_ptr(), B, H, H if H_kv is None else H_kv, N, d,
+                                             int(bool(is_causal)), PV_MODES[pv_mode],
                                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                              _stream(stream))
     _check(st, "sage_test_attn_from_workspace")

@@ -35,20 +35,20 @@ struct WsLayout {
   size_t total;
 };
 
-WsLayout make_layout(bool varlen, int B, int H, int N, int64_t T, int d, bool fp8) {
+WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d, bool fp8) {
   const int64_t tokens = varlen ? (int64_t)H * T : (int64_t)B * H * N;
-  const int64_t E = tokens * d;
+  const int64_t ktokens = varlen ? (int64_t)Hkv * T : (int64_t)B * Hkv * N;
   const int64_t nqb = ceil_div64(N, sage::kQBlock), nkb = ceil_div64(N, sage::kKBlock);
-  const int64_t vtiles = varlen ? (int64_t)H * sage::vtiles_per_head_varlen(T, B) : (int64_t)B * H * nkb;
+  const int64_t vtiles = varlen ? (int64_t)Hkv * sage::vtiles_per_head_varlen(T, B) : (int64_t)B * Hkv * nkb;
   const size_t sizes[8] = {
-      (size_t)E,
-      (size_t)E,
+      (size_t)(tokens * d),
+      (size_t)(ktokens * d),
       sizeof(float) * (size_t)B * H * nqb,
-      sizeof(float) * (size_t)B * H * nkb,
-      sizeof(float) * (size_t)B * H * d,
+      sizeof(float) * (size_t)B * Hkv * nkb,
+      sizeof(float) * (size_t)B * Hkv * d,
       (size_t)vtiles * sage::kKBlock * d * (fp8 ? 1 : 2),
-      fp8 ? sizeof(float) * (size_t)B * H * d : 0,
-      sizeof(long long) * (size_t)B * H * d,
+      fp8 ? sizeof(float) * (size_t)B * Hkv * d : 0,
+      sizeof(long long) * (size_t)B * Hkv * d,
   };
   WsLayout L;
   size_t cur = 0;
@@ -59,6 +59,9 @@ WsLayout make_layout(bool varlen, int B, int H, int N, int64_t T, int d, bool fp
   L.total = cur;
   return L;
 }
+
+// K/V heads: 1 <= Hkv <= H and Hkv divides H (grouped-query / multi-query).
+inline bool kv_heads_ok(int H, int Hkv) { return Hkv >= 1 && Hkv <= H && H % Hkv == 0; }
 
 sage_status_t check_dims(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARGUMENT;
@@ -92,22 +95,32 @@ sage_status_t finish(hipStream_t st) {
   return SAGE_OK;
 }
 
-// Shared body of the dense and varlen forward.
-sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o, const SeqGeom& g, bool varlen,
-                           int is_causal, sage_pv_mode_t pv_mode, float sm_scale, void* workspace,
-                           size_t workspace_bytes, sage_stream_t stream) noexcept {
+// Shared body of the dense and varlen forward.  g: geometry of Q and O; K and V
+// have Hkv heads over the same sequences.
+sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o, float* lse, const SeqGeom& g,
+                           int Hkv, bool varlen, int is_causal, sage_pv_mode_t pv_mode, float sm_scale,
+                           void* workspace, size_t workspace_bytes, sage_stream_t stream) noexcept {
   if (!q || !k || !v || !o || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!kv_heads_ok(g.H, Hkv)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return SAGE_ERR_INVALID_ARGUMENT;
   if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
   float sm;
   if (!resolve_sm_scale(sm_scale, g.d, &sm)) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
-  const WsLayout L = make_layout(varlen, g.B, g.H, g.N, g.T, g.d, fp8);
+  const WsLayout L = make_layout(varlen, g.B, g.H, Hkv, g.N, g.T, g.d, fp8);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
-  const size_t tensor_bytes = (size_t)(varlen ? (int64_t)g.H * g.T : (int64_t)g.B * g.H * g.N) * g.d * 2;
-  if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, tensor_bytes) ||
-      overlaps(o, tensor_bytes, v, tensor_bytes) || overlaps(o, tensor_bytes, workspace, L.total))
+  const int64_t rows = varlen ? (int64_t)g.H * g.T : (int64_t)g.B * g.H * g.N;
+  const size_t tensor_bytes = (size_t)rows * g.d * 2;
+  const size_t kv_bytes = tensor_bytes / (size_t)g.H * (size_t)Hkv;
+  const size_t lse_bytes = lse ? (size_t)rows * sizeof(float) : 0;
+  if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, kv_bytes) ||
+      overlaps(o, tensor_bytes, v, kv_bytes) || overlaps(o, tensor_bytes, workspace, L.total))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (lse && (overlaps(lse, lse_bytes, o, tensor_bytes) || overlaps(lse, lse_bytes, q, tensor_bytes) ||
+              overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
+              overlaps(lse, lse_bytes, workspace, L.total)))
     return SAGE_ERR_INVALID_ARGUMENT;
   if (tensor_bytes == 0) return SAGE_OK;  // varlen with no tokens at all
 
@@ -122,10 +135,12 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   float* vs = reinterpret_cast<float*>(ws + L.off[6]);
   long long* colsum = reinterpret_cast<long long*>(ws + L.off[7]);
 
-  sage::launch_quant_qk(g, q, k, sm, q8, k8, qs, ks, km, colsum, st);
-  if (fp8) sage::launch_v_scale(g, v, vs, st);
-  sage::launch_v_prepare(g, v, vs, fp8, /*rowmajor=*/false, vp, st);
-  sage::AttnArgs a{q8, k8, qs, ks, vp, vs, static_cast<uint16_t*>(o), g};
+  SeqGeom gk = g;
+  gk.H = Hkv;
+  sage::launch_quant_qk(g, gk, q, k, sm, q8, k8, qs, ks, km, colsum, st);
+  if (fp8) sage::launch_v_scale(gk, v, vs, st);
+  sage::launch_v_prepare(gk, v, vs, fp8, /*rowmajor=*/false, vp, st);
+  sage::AttnArgs a{q8, k8, qs, ks, vp, vs, static_cast<uint16_t*>(o), lse, g, g.H / Hkv};
   sage::launch_attn(a, is_causal != 0, fp8, st);
   return finish(st);
 }
@@ -186,7 +201,7 @@ sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, i
   if (workspace_bytes < sage_quant_qk_workspace_size(g.B, H, d)) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   if (cu_seqlens && total_tokens == 0) return SAGE_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  sage::launch_quant_qk(g, q, k, sm, q_int8, k_int8, q_scale, k_scale, k_mean,
+  sage::launch_quant_qk(g, g, q, k, sm, q_int8, k_int8, q_scale, k_scale, k_mean,
                         static_cast<long long*>(workspace), st);
   return finish(st);
 }
@@ -213,61 +228,65 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
   return finish(st);
 }
 
-size_t sage_attn_workspace_size(int B, int H, int N, int d, sage_pv_mode_t pv_mode) {
-  if (check_dims(B, H, N, d) != SAGE_OK) return 0;
+size_t sage_attn_workspace_size(int B, int H, int H_kv, int N, int d, sage_pv_mode_t pv_mode) {
+  if (check_dims(B, H, N, d) != SAGE_OK || !kv_heads_ok(H, H_kv)) return 0;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
-  return make_layout(false, B, H, N, 0, d, pv_mode == SAGE_PV_FP8_E4M3).total;
+  return make_layout(false, B, H, H_kv, N, 0, d, pv_mode == SAGE_PV_FP8_E4M3).total;
 }
 
-sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, int B, int H, int N, int d,
-                            sage_layout_t layout, int is_causal, sage_pv_mode_t pv_mode, float sm_scale,
-                            void* workspace, size_t workspace_bytes, sage_stream_t stream) {
+sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                            int H_kv, int N, int d, sage_layout_t layout, int is_causal, sage_pv_mode_t pv_mode,
+                            float sm_scale, void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
   const sage_status_t s = check_dims(B, H, N, d);
   if (s != SAGE_OK) return s;
   const SeqGeom g{nullptr, B, H, N, d, 0};
-  return attn_forward(q, k, v, o, g, false, is_causal, pv_mode, sm_scale, workspace, workspace_bytes, stream);
+  return attn_forward(q, k, v, o, lse, g, H_kv, false, is_causal, pv_mode, sm_scale, workspace, workspace_bytes,
+                      stream);
 }
 
-size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H, int d,
+size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H, int H_kv, int d,
                                        sage_pv_mode_t pv_mode) {
-  if (nseq < 1 || total_tokens < 0 || check_dims(nseq, H, max_seqlen, d) != SAGE_OK) return 0;
+  if (nseq < 1 || total_tokens < 0 || check_dims(nseq, H, max_seqlen, d) != SAGE_OK || !kv_heads_ok(H, H_kv))
+    return 0;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
-  return make_layout(true, nseq, H, max_seqlen, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3).total;
+  return make_layout(true, nseq, H, H_kv, max_seqlen, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3).total;
 }
 
-sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o, const int32_t* cu_seqlens,
-                                   int nseq, int max_seqlen, int64_t total_tokens, int H, int d, int is_causal,
-                                   sage_pv_mode_t pv_mode, float sm_scale, void* workspace, size_t workspace_bytes,
-                                   sage_stream_t stream) {
+sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   const int32_t* cu_seqlens, int nseq, int max_seqlen, int64_t total_tokens, int H,
+                                   int H_kv, int d, int is_causal, sage_pv_mode_t pv_mode, float sm_scale,
+                                   void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   SeqGeom g;
   const sage_status_t s = varlen_geom(cu_seqlens, nseq, max_seqlen, total_tokens, H, d, &g);
   if (s != SAGE_OK) return s;
-  return attn_forward(q, k, v, o, g, true, is_causal, pv_mode, sm_scale, workspace, workspace_bytes, stream);
+  return attn_forward(q, k, v, o, lse, g, H_kv, true, is_causal, pv_mode, sm_scale, workspace, workspace_bytes,
+                      stream);
 }
 
-sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int N, int64_t total_tokens, int d,
+sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int N, int64_t total_tokens, int d,
                                          sage_pv_mode_t pv_mode, size_t offsets_out[8]) {
   if (!offsets_out) return SAGE_ERR_INVALID_ARGUMENT;
-  if (check_dims(B, H, N, d) != SAGE_OK) return SAGE_ERR_INVALID_ARGUMENT;
+  if (check_dims(B, H, N, d) != SAGE_OK || !kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
   if (varlen && total_tokens < 0) return SAGE_ERR_INVALID_ARGUMENT;
-  const WsLayout L = make_layout(varlen != 0, B, H, N, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3);
+  const WsLayout L = make_layout(varlen != 0, B, H, H_kv, N, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3);
   for (int i = 0; i < 7; ++i) offsets_out[i] = L.off[i];
   offsets_out[7] = L.total;
   return SAGE_OK;
 }
 
-sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int N, int d, int is_causal,
+sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int N, int d, int is_causal,
                                             sage_pv_mode_t pv_mode, const void* workspace, size_t workspace_bytes,
                                             sage_stream_t stream) {
   const sage_status_t s = check_dims(B, H, N, d);
   if (s != SAGE_OK) return s;
+  if (!kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!o || !workspace || !aligned16(o) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
     return SAGE_ERR_INVALID_ARGUMENT;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
-  const WsLayout L = make_layout(false, B, H, N, 0, d, fp8);
+  const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, fp8);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const size_t tensor_bytes = (size_t)B * H * N * d * 2;
   if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -276,7 +295,7 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int N, int d,
   sage::AttnArgs a{reinterpret_cast<const int8_t*>(ws + L.off[0]), reinterpret_cast<const int8_t*>(ws + L.off[1]),
                    reinterpret_cast<const float*>(ws + L.off[2]), reinterpret_cast<const float*>(ws + L.off[3]),
                    reinterpret_cast<const uint8_t*>(ws + L.off[5]), reinterpret_cast<const float*>(ws + L.off[6]),
-                   static_cast<uint16_t*>(o), g};
+                   static_cast<uint16_t*>(o), nullptr, g, H / H_kv};
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   sage::launch_attn(a, is_causal != 0, fp8, st);
   return finish(st);

@@ -464,18 +464,27 @@ void attn_fwd_kernel(AttnArgs a) {
   const int wq_hi = min(wq_lo + 31, n - 1);
   const bool wave_rows = wq_lo < n;
 
+  // K/V head of this query head (grouped-query attention; kv_group = 1 otherwise)
+  SeqGeom gk = g;
+  gk.H = g.H / a.kv_group;
+  const int hk = h / a.kv_group;
+  const int64_t hsk = (int64_t)b * gk.H + hk;
+  int64_t krow0;
+  int kn;
+  hs_rows(gk, b, hk, krow0, kn);  // kn == n: same sequence
+
   const int kend = CAUSAL ? min(n, q0 + kAttnRows) : n;
   const int ntiles = ceil_div(kend, kKBlock);
-  const int8_t* kbase = a.k + row0 * D;
+  const int8_t* kbase = a.k + krow0 * D;
   const int kbytes = n * D;
-  const uint8_t* vbase = a.v_packed + vtile_index(g, b, h, 0) * G::VBYTES;
+  const uint8_t* vbase = a.v_packed + vtile_index(gk, b, hk, 0) * G::VBYTES;
   const int vbytes = ceil_div(n, kKBlock) * G::VBYTES;
   constexpr int L = G::KI + G::VI;  // DMA instructions per group-A wave per tile
 
   WaveCtx<D, FP8> c;
   load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
   const float dq = load_uniform(a.q_scale, hs * nqb + wq_lo / kQBlock);
-  const float* __restrict__ ksc = a.k_scale + hs * nkb;
+  const float* __restrict__ ksc = a.k_scale + hsk * nkb;
   c.m_run = -__builtin_inff();
   c.l_run = 0.f;
 #pragma unroll
@@ -536,6 +545,11 @@ void attn_fwd_kernel(AttnArgs a) {
   const float l_tot = pair_sum(c.l_run);
   if (!wave_rows || qrow >= n) return;
   const float inv = 1.f / l_tot;
+  if (a.lse && gg == 0) {
+    // natural-log sum of exp of the row's scaled scores: m is in log2 units
+    const float log2_l = __builtin_log2f(l_tot) - (FP8 ? kLog2E4M3Max : 0.f);
+    a.lse[row0 + qrow] = (c.m_run + log2_l) * 0.6931471805599453f;
+  }
   uint16_t* __restrict__ orow = a.o + (row0 + qrow) * D;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
@@ -546,7 +560,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) f[j] = c.O[dt][4 * q4 + j] * inv;
       if (FP8) {
-        const float4 vs = *reinterpret_cast<const float4*>(a.v_scale + hs * D + d);  // per-lane d
+        const float4 vs = *reinterpret_cast<const float4*>(a.v_scale + hsk * D + d);  // per-lane d
         f[0] *= vs.x;
         f[1] *= vs.y;
         f[2] *= vs.z;

@@ -340,26 +340,27 @@ void launch_zero(void* p, size_t bytes, hipStream_t st) {
                      reinterpret_cast<v4i*>(p), n16);
 }
 
-void launch_quant_qk(const SeqGeom& g, const void* q, const void* k, float sm_scale, int8_t* q_int8,
-                     int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, long long* colsum,
-                     hipStream_t st) {
+void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, float sm_scale,
+                     int8_t* q_int8, int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean,
+                     long long* colsum, hipStream_t st) {
+  // gq: Q's geometry (H query heads); gk: K's (its own head count), same sequences
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
   const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
-  launch_zero(colsum, sizeof(long long) * (size_t)g.B * g.H * g.d, st);
-  if (g.d == 128) {
-    hipLaunchKernelGGL((k_colsum_kernel<128>), hs_grid(g, kColsumChunk), dim3(kThreads), 0, st, k16, g,
+  launch_zero(colsum, sizeof(long long) * (size_t)gk.B * gk.H * gk.d, st);
+  if (gq.d == 128) {
+    hipLaunchKernelGGL((k_colsum_kernel<128>), hs_grid(gk, kColsumChunk), dim3(kThreads), 0, st, k16, gk,
                        reinterpret_cast<unsigned long long*>(colsum));
-    hipLaunchKernelGGL((quant_block_kernel<128, kQBlock, false>), hs_grid(g, kQBlock), dim3(kThreads), 0, st,
-                       q16, g, (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);
-    hipLaunchKernelGGL((quant_block_kernel<128, kKBlock, true>), hs_grid(g, kKBlock), dim3(kThreads), 0, st,
-                       k16, g, (const long long*)colsum, 1.0f, k_int8, k_scale, k_mean);
+    hipLaunchKernelGGL((quant_block_kernel<128, kQBlock, false>), hs_grid(gq, kQBlock), dim3(kThreads), 0, st,
+                       q16, gq, (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);
+    hipLaunchKernelGGL((quant_block_kernel<128, kKBlock, true>), hs_grid(gk, kKBlock), dim3(kThreads), 0, st,
+                       k16, gk, (const long long*)colsum, 1.0f, k_int8, k_scale, k_mean);
   } else {
-    hipLaunchKernelGGL((k_colsum_kernel<64>), hs_grid(g, kColsumChunk), dim3(kThreads), 0, st, k16, g,
+    hipLaunchKernelGGL((k_colsum_kernel<64>), hs_grid(gk, kColsumChunk), dim3(kThreads), 0, st, k16, gk,
                        reinterpret_cast<unsigned long long*>(colsum));
-    hipLaunchKernelGGL((quant_block_kernel<64, kQBlock, false>), hs_grid(g, kQBlock), dim3(kThreads), 0, st,
-                       q16, g, (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);
-    hipLaunchKernelGGL((quant_block_kernel<64, kKBlock, true>), hs_grid(g, kKBlock), dim3(kThreads), 0, st,
-                       k16, g, (const long long*)colsum, 1.0f, k_int8, k_scale, k_mean);
+    hipLaunchKernelGGL((quant_block_kernel<64, kQBlock, false>), hs_grid(gq, kQBlock), dim3(kThreads), 0, st,
+                       q16, gq, (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);
+    hipLaunchKernelGGL((quant_block_kernel<64, kKBlock, true>), hs_grid(gk, kKBlock), dim3(kThreads), 0, st,
+                       k16, gk, (const long long*)colsum, 1.0f, k_int8, k_scale, k_mean);
   }
 }
 

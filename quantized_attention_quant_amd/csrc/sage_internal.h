@@ -8,17 +8,20 @@ namespace sage {
 
 struct AttnArgs {
   const int8_t* q;         // Q codes, same layout as the fp16 input
-  const int8_t* k;         // K codes
+  const int8_t* k;         // K codes (H / kv_group heads)
   const float* q_scale;    // [B][H][nqb], softmax scale folded in
-  const float* k_scale;    // [B][H][nkb]
-  const uint8_t* v_packed; // packed V tiles (fp16 or e4m3)
-  const float* v_scale;    // [B][H][d] (FP8 mode)
+  const float* k_scale;    // [B][Hkv][nkb]
+  const uint8_t* v_packed; // packed V tiles (fp16 or e4m3), Hkv heads
+  const float* v_scale;    // [B][Hkv][d] (FP8 mode)
   uint16_t* o;             // fp16 output, same layout as the input
-  SeqGeom g;
+  float* lse;              // optional fp32 log-sum-exp per query row, or nullptr
+  SeqGeom g;               // geometry of Q and O (H query heads)
+  int kv_group;            // query heads per K/V head: K/V head of h is h / kv_group
 };
 
 void launch_zero(void* p, size_t bytes, hipStream_t st);
-void launch_quant_qk(const SeqGeom& g, const void* q, const void* k, float sm_scale, int8_t* q_int8,
+void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, float sm_scale,
+                     int8_t* q_int8,
                      int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, long long* colsum,
                      hipStream_t st);
 void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st);

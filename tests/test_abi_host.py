@@ -59,14 +59,23 @@ def test_workspace_sizes():
     assert offs[7] == w8
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs)
+    # grouped K/V heads shrink every K/V region; invalid groupings give 0
+    g = sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16", H_kv=1)
+    assert 0 < g < sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16")
+    assert sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16", H_kv=3) == 0
+    assert sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16", H_kv=8) == 0
+    assert sage.sage_attn_varlen_workspace_size(3, 200, 271, 4, 128, "fp16", H_kv=2) > 0
+    offs = sage.sage_test_workspace_layout(False, 1, 4, 256, 0, 64, "fp16", H_kv=2)
+    assert offs[1] - offs[0] == 4 * 256 * 64 and offs[2] - offs[1] == 2 * 256 * 64
 
 
 def _fwd(**over):
-    a = dict(q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, o=ALIGNED * 4, B=1, H=2, N=256, d=64, layout=0,
-             causal=0, pv=0, sm=0.0, ws=ALIGNED * 8, wsb=1 << 30, stream=None)
+    a = dict(q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, o=ALIGNED * 4, lse=None, B=1, H=2, Hkv=2, N=256, d=64,
+             layout=0, causal=0, pv=0, sm=0.0, ws=ALIGNED * 8, wsb=1 << 30, stream=None)
     a.update(over)
-    return sage.lib().sage_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["B"], a["H"], a["N"], a["d"], a["layout"],
-                                    a["causal"], a["pv"], a["sm"], a["ws"], a["wsb"], a["stream"])
+    return sage.lib().sage_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
+                                    a["d"], a["layout"], a["causal"], a["pv"], a["sm"], a["ws"], a["wsb"],
+                                    a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -87,6 +96,11 @@ def _fwd(**over):
     (dict(sm=float("inf")), INVALID),
     (dict(wsb=100), WS_SMALL),
     (dict(o=ALIGNED), INVALID),              # output aliases q
+    (dict(Hkv=0), INVALID),
+    (dict(Hkv=3), INVALID),                  # does not divide H
+    (dict(Hkv=4), INVALID),                  # more K/V heads than query heads
+    (dict(lse=ALIGNED * 4 + 2), INVALID),    # lse misaligned
+    (dict(lse=ALIGNED * 4), INVALID),        # lse overlaps the output
 ])
 def test_attn_fwd_rejects(over, status):
     assert _fwd(**over) == status
@@ -95,17 +109,19 @@ def test_attn_fwd_rejects(over, status):
 def test_varlen_rejects():
     L = sage.lib()
     f = L.sage_attn_varlen_fwd
-    args = [ALIGNED, ALIGNED * 2, ALIGNED * 3, ALIGNED * 4, ALIGNED * 5, 3, 128, 300, 2, 64, 1, 0, 0.0,
+    args = [ALIGNED, ALIGNED * 2, ALIGNED * 3, ALIGNED * 4, None, ALIGNED * 5, 3, 128, 300, 2, 2, 64, 1, 0, 0.0,
             ALIGNED * 8, 1 << 30, None]
-    bad = list(args); bad[4] = None                 # cu_seqlens
+    bad = list(args); bad[5] = None                 # cu_seqlens
     assert f(*bad) == INVALID
-    bad = list(args); bad[5] = 0                    # nseq
+    bad = list(args); bad[6] = 0                    # nseq
     assert f(*bad) == INVALID
-    bad = list(args); bad[7] = 3 * 128 + 1          # more tokens than nseq * max_seqlen
+    bad = list(args); bad[8] = 3 * 128 + 1          # more tokens than nseq * max_seqlen
     assert f(*bad) == INVALID
-    bad = list(args); bad[7] = -1
+    bad = list(args); bad[8] = -1
     assert f(*bad) == INVALID
-    bad = list(args); bad[14] = 10
+    bad = list(args); bad[10] = 3                   # H_kv does not divide H
+    assert f(*bad) == INVALID
+    bad = list(args); bad[16] = 10
     assert f(*bad) == WS_SMALL
 
 
@@ -122,7 +138,8 @@ def test_quant_rejects():
     st = L.sage_test_qk_tiles(ALIGNED, ALIGNED * 2, 1, 1, 128, 64, ALIGNED * 3, 0, ALIGNED * 4, None)
     assert st == INVALID
     arr = (ctypes.c_size_t * 8)()
-    assert L.sage_test_workspace_layout(0, 1, 1, 128, 0, 80, 0, arr) == INVALID
+    assert L.sage_test_workspace_layout(0, 1, 1, 1, 128, 0, 80, 0, arr) == INVALID
+    assert L.sage_test_workspace_layout(0, 1, 4, 3, 128, 0, 64, 0, arr) == INVALID
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

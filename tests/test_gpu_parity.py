@@ -219,6 +219,90 @@ def test_deterministic_and_workspace_matches_quant():
             assert (wsn[offs[6]:offs[6] + 4 * 512].view(np.float32) == host(vs).ravel()).all()
 
 
+LSE_ABS = 2e-3  # natural-log units; the kernel keeps m and l in fp32
+
+
+# Grouped-query heads (H_kv < H) and the log-sum-exp output, against the oracle
+# run on K/V repeated to H heads (the same computation per query head).
+GQA = [(4, 2, 65, 64), (4, 1, 257, 128), (6, 3, 200, 64), (2, 2, 129, 128)]
+
+
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("H,H_kv,n,d", GQA)
+def test_gqa_and_lse(H, H_kv, n, d, causal, pv_mode):
+    say(f"case gqa H={H} H_kv={H_kv} n={n} d={d} causal={causal} pv={pv_mode}")
+    B, grp = 2, H // H_kv
+    x = workloads.generate_custom(300 + H * 10 + H_kv + n, B, H, n, d, k_bias=3.0, q_bias=1.0)
+    q = x.q
+    k = np.ascontiguousarray(x.k[:, :H_kv])
+    v = np.ascontiguousarray(x.v[:, :H_kv])
+    ws = torch.empty(sage.sage_attn_workspace_size(B, H, n, d, pv_mode, H_kv=H_kv), dtype=torch.uint8,
+                     device="cuda")
+    o, lse = sage.sage_attn_fwd(dev(q), dev(k), dev(v), is_causal=causal, pv_mode=pv_mode, workspace=ws,
+                                return_lse=True)
+    o, lse, wsn = host(o), host(lse), host(ws)
+    # K codes per K/V head, bit-exact (smoothing and blocks per K/V head)
+    ref = O.quant_qk_dense(q, k)
+    offs = sage.sage_test_workspace_layout(False, B, H, n, 0, d, pv_mode, H_kv=H_kv)
+    nk8 = B * H_kv * n * d
+    assert (wsn[offs[1]:offs[1] + nk8].view(np.int8) == ref["k_int8"].ravel()).all()
+    assert (wsn[offs[0]:offs[0] + B * H * n * d].view(np.int8) == ref["q_int8"].ravel()).all()
+    k_rep, v_rep = np.repeat(k, grp, axis=1), np.repeat(v, grp, axis=1)
+    quant = O.quant_qk_dense(q, k_rep)
+    vc, vs = O.quant_v_fp8(v_rep)
+    rows = np.arange(n)
+    for b in range(B):
+        for h in range(H):
+            qi, qs, ki, ks = O.head_views_dense(quant, b, h)
+            if pv_mode == "fp8":
+                o1 = O.sage_attention_rows(qi, qs, ki, ks, vc[b, h], rows, causal, "fp8", vs[b, h])
+            else:
+                o1 = O.sage_attention_rows(qi, qs, ki, ks, v_rep[b, h], rows, causal, "fp16")
+            o2 = O.sdpa_fp64_rows(q[b, h], k_rep[b, h], v_rep[b, h], rows, causal)
+            check_out(o[b, h], o1, o2, f"gqa b={b} h={h}")
+            want = O.score_lse_rows(qi, qs, ki, ks, rows, causal)
+            err = np.abs(lse[b, h].astype(np.float64) - want).max()
+            assert err <= LSE_ABS, (b, h, err)
+
+
+def test_gqa_varlen_with_lse():
+    lens = [1, 65, 300, 0, 129]
+    H, H_kv, d = 4, 2, 128
+    cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, mx = int(cu_h[-1]), max(lens)
+    x = workloads.generate_custom(55, 1, H, T, d, k_bias=3.0, q_bias=1.0)
+    q = np.ascontiguousarray(x.q[0])
+    k = np.ascontiguousarray(x.k[0, :H_kv])
+    v = np.ascontiguousarray(x.v[0, :H_kv])
+    cu = dev(cu_h)
+    for pv_mode in ("fp16", "fp8"):
+        for causal in (False, True):
+            say(f"case gqa varlen pv={pv_mode} causal={causal}")
+            o, lse = sage.sage_attn_varlen_fwd(dev(q), dev(k), dev(v), cu, mx, is_causal=causal, pv_mode=pv_mode,
+                                               return_lse=True)
+            o, lse = host(o), host(lse)
+            k_rep, v_rep = np.repeat(k, 2, axis=0), np.repeat(v, 2, axis=0)
+            quant = O.quant_qk_varlen(q, k_rep, cu_h)
+            for i, n in enumerate(lens):
+                if n == 0:
+                    continue
+                a0 = int(cu_h[i])
+                rows = np.arange(n)
+                for h in range(H):
+                    qi, qs, ki, ks = O.head_views_varlen(quant, cu_h, i, h)
+                    vv = v_rep[h, a0:a0 + n]
+                    if pv_mode == "fp8":
+                        vc, vs = O.quant_v_fp8(vv)
+                        o1 = O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs)
+                    else:
+                        o1 = O.sage_attention_rows(qi, qs, ki, ks, vv, rows, causal, "fp16")
+                    o2 = O.sdpa_fp64_rows(q[h, a0:a0 + n], k_rep[h, a0:a0 + n], vv, rows, causal)
+                    check_out(o[h, a0:a0 + n], o1, o2, f"gqa varlen seq={i} h={h}")
+                    want = O.score_lse_rows(qi, qs, ki, ks, rows, causal)
+                    assert np.abs(lse[h, a0:a0 + n].astype(np.float64) - want).max() <= LSE_ABS
+
+
 def test_varlen_small_all_rows():
     lens = [1, 63, 64, 65, 130, 0, 257]
     for d in (64, 128):

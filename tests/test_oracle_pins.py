@@ -276,6 +276,33 @@ def test_zero_query_gives_mean_of_visible_values():
         assert (outc[r].view(np.uint16) == want.view(np.uint16)).all()
 
 
+def test_score_lse_pins():
+    """LSE oracle: against scipy's logsumexp on independently formed scores,
+    the closed forms log(#visible) for Q = 0 and s_00 for causal row 0."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(21)
+    n, d = 200, 64
+    q, k = (rng.standard_normal((n, d)).astype(np.float16) for _ in range(2))
+    quant = O.quant_qk_dense(q[None, None], k[None, None])
+    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+    rows = np.array([0, 1, 63, 64, 127, 128, 199])
+    for causal in (False, True):
+        got = O.score_lse_rows(qi, qs, ki, ks, rows, causal)
+        for r, i in enumerate(rows):
+            vis = np.arange(i + 1) if causal else np.arange(n)
+            s = [float(qs[i // 128]) * float(ks[j // 64]) * sum(int(a) * int(b) for a, b in zip(qi[i], ki[j]))
+                 for j in vis]
+            assert abs(got[r] - logsumexp(s)) <= 1e-12 * max(1.0, abs(got[r]))
+    # causal row 0 sees one key: lse = its score
+    s00 = float(qs[0]) * float(ks[0]) * float(qi[0].astype(np.int64) @ ki[0].astype(np.int64))
+    assert O.score_lse_rows(qi, qs, ki, ks, [0], True)[0] == s00
+    # Q = 0: every score is 0, lse = log(#visible keys)
+    z = O.quant_qk_dense(np.zeros((1, 1, n, d), np.float16), k[None, None])
+    qz, qzs, kz, kzs = O.head_views_dense(z, 0, 0)
+    assert np.allclose(O.score_lse_rows(qz, qzs, kz, kzs, rows, True), np.log(rows + 1.0), rtol=0, atol=1e-15)
+    assert np.allclose(O.score_lse_rows(qz, qzs, kz, kzs, rows, False), np.log(n), rtol=0, atol=1e-15)
+
+
 def test_lossless_grid_matches_exact_attention():
     rng = np.random.default_rng(15)
     n, d = 320, 64
