@@ -41,16 +41,22 @@ __global__ __launch_bounds__(kThreads) void k_colsum_kernel(const uint16_t* __re
   const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
   // fp64 partial sums are exact: every fp16 value is a multiple of 2^-24 below
   // 2^16 in magnitude, and a thread adds at most kColsumChunk / RPP of them
+  constexpr int ITER = kColsumChunk / RPP;
+  v4i raw[ITER];  // all loads in flight before the adds
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int t = t0 + rr + i * RPP;
+    raw[i] = (t < t1) ? *reinterpret_cast<const v4i*>(k + (row0 + t) * D + cg * 8) : v4i{0, 0, 0, 0};
+  }
   double acc[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
-  for (int t = t0 + rr; t < t1; t += RPP) {
-    const v4i raw = *reinterpret_cast<const v4i*>(k + (row0 + t) * D + cg * 8);
+#pragma unroll
+  for (int i = 0; i < ITER; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w = (uint32_t)raw[j];
+      const uint32_t w = (uint32_t)raw[i][j];
       acc[2 * j] += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
       acc[2 * j + 1] += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
     }
-  }
   static_assert(kColsumChunk / RPP <= 8192, "fp64 partial sums must stay exact");
   __shared__ int64_t red[RPP][D];
 #pragma unroll
@@ -117,6 +123,13 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* _
   if (t0 >= n) return;
   const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
   const int64_t hs = (int64_t)b * g.H + h;
+  // all of the block's loads first (raw fp16, 16 bytes per pass and thread)
+  v4i raw[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + rr + p * RPP;
+    raw[p] = (t < n) ? *reinterpret_cast<const v4i*>(x16 + (row0 + t) * D + cg * 8) : v4i{0, 0, 0, 0};
+  }
   float shift[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) shift[j] = 0.f;
@@ -132,27 +145,24 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* _
 #pragma unroll
     for (int j = 0; j < 8; ++j) shift[j] = km_s[cg * 8 + j];
   }
-  float x[PASSES][8];
+  // x = fp32(fp16) - shift; rows past n are zero (their codes are not stored)
+  auto unpack = [&](int p, float (&x)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = (uint32_t)raw[p][j];
+      x[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)) - shift[2 * j];
+      x[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)) - shift[2 * j + 1];
+    }
+  };
   float amax = 0.f;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
-    const int t = t0 + rr + p * RPP;
-    if (t < n) {
-      const v4i raw = *reinterpret_cast<const v4i*>(x16 + (row0 + t) * D + cg * 8);
+    if (t0 + rr + p * RPP < n) {
+      float x[8];
+      unpack(p, x);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t w = (uint32_t)raw[j];
-        const float lo = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-        const float hi = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-        x[p][2 * j] = lo - shift[2 * j];
-        x[p][2 * j + 1] = hi - shift[2 * j + 1];
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) x[p][j] = 0.f;
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
     }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[p][j]));
   }
   amax = block_max256(amax);
   const float s = amax / kInt8Max;
@@ -163,10 +173,10 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* _
     if (t < n) {
       uint2 w = {0u, 0u};  // an all-zero block (s = 0) has all codes 0
       if (s > 0.f) {
-        w.x = pack4_i8(int8_code(x[p][0], s, r), int8_code(x[p][1], s, r), int8_code(x[p][2], s, r),
-                       int8_code(x[p][3], s, r));
-        w.y = pack4_i8(int8_code(x[p][4], s, r), int8_code(x[p][5], s, r), int8_code(x[p][6], s, r),
-                       int8_code(x[p][7], s, r));
+        float x[8];
+        unpack(p, x);
+        w.x = pack4_i8(int8_code(x[0], s, r), int8_code(x[1], s, r), int8_code(x[2], s, r), int8_code(x[3], s, r));
+        w.y = pack4_i8(int8_code(x[4], s, r), int8_code(x[5], s, r), int8_code(x[6], s, r), int8_code(x[7], s, r));
       }
       *reinterpret_cast<uint2*>(codes + (row0 + t) * D + cg * 8) = w;
     }
@@ -192,16 +202,22 @@ __global__ __launch_bounds__(kThreads) void v_absmax_kernel(const uint16_t* __re
   if (t0 >= n) return;
   const int t1 = min(n, t0 + kColsumChunk);
   const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
+  constexpr int ITER = kColsumChunk / RPP;
+  v4i raw[ITER];  // all loads in flight before the reduction
+#pragma unroll
+  for (int i = 0; i < ITER; ++i) {
+    const int t = t0 + rr + i * RPP;
+    raw[i] = (t < t1) ? *reinterpret_cast<const v4i*>(v + (row0 + t) * D + cg * 8) : v4i{0, 0, 0, 0};
+  }
   float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int t = t0 + rr; t < t1; t += RPP) {
-    const v4i raw = *reinterpret_cast<const v4i*>(v + (row0 + t) * D + cg * 8);
+#pragma unroll
+  for (int i = 0; i < ITER; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t w = (uint32_t)raw[j];
+      const uint32_t w = (uint32_t)raw[i][j];
       m[2 * j] = fmaxf(m[2 * j], fabsf((float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu))));
       m[2 * j + 1] = fmaxf(m[2 * j + 1], fabsf((float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16))));
     }
-  }
   __shared__ float red[RPP][D];
 #pragma unroll
   for (int j = 0; j < 8; ++j) red[rr][cg * 8 + j] = m[j];
