@@ -434,8 +434,14 @@ __device__ __forceinline__ void wait_tiles(int pending) {
     wait_dma<0>();
 }
 
+// d=64 fits 128 VGPRs, so two workgroups share a CU (four waves per SIMD) and
+// their independent phases fill each other's stalls; d=128 needs ~180.
+template <int D>
+constexpr int kAttnWavesPerSimd = (D == 64) ? 4 : 2;
+
 template <int D, bool FP8, bool CAUSAL>
-__global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads), amdgpu_waves_per_eu(2, 2)))
+__global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads),
+                          amdgpu_waves_per_eu(kAttnWavesPerSimd<D>, kAttnWavesPerSimd<D>)))
 void attn_fwd_kernel(AttnArgs a) {
   constexpr int DT = D / 32;  // 32-wide d tiles of the output
   using G = TileGeom<D, FP8, kThreads>;  // tiles are streamed by the 4 waves of group A
