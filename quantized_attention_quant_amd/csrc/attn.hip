@@ -505,8 +505,10 @@ void attn_fwd_kernel(AttnArgs a) {
     const int first = min(kAhead, ntiles);
     for (int t = 0; t < first; ++t)
       issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, t, smem + t * G::STAGE, w, lane);
-    wait_tiles<L>(first - 1);  // tile 0 landed
   }
+  // the first tiles and this wave's Q̂ fragments have landed; an empty queue
+  // here also lets the compiler see that no later MFMA waits on the Q̂ loads
+  wait_dma<0>();
   barrier_only();
 
   // tiles this wave takes part in: 0..nact-1 (causal: keys up to its last query)
