@@ -44,7 +44,11 @@ Readings where the pages are silent (each listed in the design notes):
   * FP8 mode: V per-channel scale amax/448, codes OCP e4m3 (bias 7, max 448,
     round to nearest even, saturate to ±448); P codes are e4m3(p * 448);
     level 1 sums one tile's P̂V̂, level 2 is the running output;
-  * the row sum l is taken from the unrounded p.
+  * the row sum l is taken from the unrounded p;
+  * Q smoothing (optional): the mean of each 128-token Q block (the K-mean
+    rule applied to that block) is subtracted before the INT8 step, and the
+    part of the score it carries, sm_scale * q̄ · (k - km) with the smoothed K
+    in fp32, is added back exactly (fp64) to every score of the block's rows.
 """
 from __future__ import annotations
 
@@ -65,7 +69,7 @@ __all__ = [
     "quantize_int8_blocks", "quant_q", "quant_k", "quant_qk_dense", "quant_qk_varlen",
     "e4m3_decode", "e4m3_encode", "quant_v_fp8", "quant_v_fp8_dense", "quant_v_fp8_varlen",
     "qk_int", "sage_attention_rows", "sdpa_fp64_rows", "head_views_dense",
-    "head_views_varlen",
+    "head_views_varlen", "q_block_mean", "quant_q_smooth", "q_smooth_bias",
 ]
 
 
@@ -158,51 +162,108 @@ def quant_k(k: np.ndarray):
     return codes, scale, km
 
 
-def quant_qk_dense(q: np.ndarray, k: np.ndarray, sm_scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+# ----------------------------------------------------------------------------
+# Q smoothing ([DT] "SageAttention 2": Q is smoothed too, for a more accurate
+# QKᵀ; [PS] SageAttention2 bullets: Q is normalised as well so that the
+# attention result is not distorted)
+# ----------------------------------------------------------------------------
+def q_block_mean(q: np.ndarray) -> np.ndarray:
+    """Per 128-token block channel mean of Q: fp16 [..., n, d] -> fp32
+    [..., ceil(n/128), d].  Each block (the last one partial) uses the exact
+    mean rule of the K mean over its own tokens."""
+    n = q.shape[-2]
+    return np.stack([k_token_mean(q[..., b0:min(n, b0 + Q_BLOCK), :]) for b0 in range(0, n, Q_BLOCK)], axis=-2)
+
+
+def quant_q_smooth(q: np.ndarray, sm_scale: np.float32):
+    """Q smoothed by its block mean, then per 128-token block INT8.
+
+    x = fp32(q) - q̄ (fp32, the block's own mean), quantised like Q without
+    smoothing; sm_scale is folded into the emitted scale.  Returns (codes
+    int8, scale fp32 per block, q̄ fp32 [..., nqb, d]).
+    """
+    n = q.shape[-2]
+    qm = q_block_mean(q)
+    x = q.astype(np.float32) - np.repeat(qm, Q_BLOCK, axis=-2)[..., :n, :]
+    codes, scale = quantize_int8_blocks(x.astype(np.float32), Q_BLOCK)
+    return codes, (scale * np.float32(sm_scale)).astype(np.float32), qm
+
+
+def q_smooth_bias(q_mean: np.ndarray, k: np.ndarray, k_mean: np.ndarray, sm_scale: float) -> np.ndarray:
+    """The score term the smoothed Q̂ leaves out, per (Q block, key), in fp64:
+
+        bias[b, j] = sm_scale · Σ_c q̄[b, c] · x[j, c],   x = fp32(k) - km,
+
+    the smoothed K in fp32 exactly as the K path forms it.  One (sequence,
+    head): q_mean [nqb, d], k fp16 [n, d], k_mean [d] -> [nqb, n].  Every
+    score of a row in block b gets bias[b, j] added before the softmax.
+    """
+    x = smooth_k(k, k_mean).astype(np.float64)
+    return float(sm_scale) * (q_mean.astype(np.float64) @ x.T)
+
+
+def quant_qk_dense(q: np.ndarray, k: np.ndarray, sm_scale: Optional[float] = None,
+                   smooth_q: bool = False) -> Dict[str, np.ndarray]:
     """Dense [B, H, N, d] fp16 inputs ([CS]: HND layout) -> INT8 tensors and scales.
 
     Output shapes: q_int8, k_int8 [B,H,N,d]; q_scale [B,H,ceil(N/128)];
-    k_scale [B,H,ceil(N/64)]; k_mean [B,H,d].
+    k_scale [B,H,ceil(N/64)]; k_mean [B,H,d]; with smooth_q also q_mean
+    [B,H,ceil(N/128),d].  K may have fewer heads than Q (its own shape).
     """
     d = q.shape[-1]
     sm = default_sm_scale(d) if not sm_scale or sm_scale <= 0 else np.float32(sm_scale)
-    qi, qs = quant_q(q, sm)
+    out = {}
+    if smooth_q:
+        qi, qs, out["q_mean"] = quant_q_smooth(q, sm)
+    else:
+        qi, qs = quant_q(q, sm)
     ki, ks, km = quant_k(k)
-    return dict(q_int8=qi, q_scale=qs, k_int8=ki, k_scale=ks, k_mean=km)
+    out.update(q_int8=qi, q_scale=qs, k_int8=ki, k_scale=ks, k_mean=km)
+    return out
 
 
 def quant_qk_varlen(q: np.ndarray, k: np.ndarray, cu_seqlens: Sequence[int],
-                    sm_scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+                    sm_scale: Optional[float] = None, smooth_q: bool = False) -> Dict[str, np.ndarray]:
     """Packed [H, T, d] inputs with sequence i on tokens [cu[i], cu[i+1]).
 
     Blocks and means never cross a sequence.  Scales and means are returned
     padded per sequence: q_scale [nseq,H,ceil(max/128)], k_scale
-    [nseq,H,ceil(max/64)], k_mean [nseq,H,d]; padding entries are NaN (no
-    value is defined there).
+    [nseq,H,ceil(max/64)], k_mean [nseq,H,d], with smooth_q also q_mean
+    [nseq,H,ceil(max/128),d]; padding entries are NaN (no value is defined
+    there).  K may have fewer heads than Q (its own shape).
     """
     H, T, d = q.shape
+    Hk = k.shape[0]
     cu = np.asarray(cu_seqlens, dtype=np.int64)
     nseq = len(cu) - 1
     lens = np.diff(cu)
-    mx = int(lens.max())
+    mx = max(int(lens.max()), 1)
     sm = default_sm_scale(d) if not sm_scale or sm_scale <= 0 else np.float32(sm_scale)
     qi = np.zeros((H, T, d), np.int8)
-    ki = np.zeros((H, T, d), np.int8)
+    ki = np.zeros((Hk, T, d), np.int8)
     qs = np.full((nseq, H, -(-mx // Q_BLOCK)), np.nan, np.float32)
-    ks = np.full((nseq, H, -(-mx // K_BLOCK)), np.nan, np.float32)
-    km = np.zeros((nseq, H, d), np.float32)
+    ks = np.full((nseq, Hk, -(-mx // K_BLOCK)), np.nan, np.float32)
+    km = np.zeros((nseq, Hk, d), np.float32)
+    qm = np.full((nseq, H, -(-mx // Q_BLOCK), d), np.nan, np.float32)
     for i in range(nseq):
         a, b = int(cu[i]), int(cu[i + 1])
         if b == a:
             continue
-        c, s = quant_q(q[:, a:b], sm)
+        if smooth_q:
+            c, s, m = quant_q_smooth(q[:, a:b], sm)
+            qm[i, :, : m.shape[-2]] = m
+        else:
+            c, s = quant_q(q[:, a:b], sm)
         qi[:, a:b] = c
         qs[i, :, : s.shape[-1]] = s
         c, s, m = quant_k(k[:, a:b])
         ki[:, a:b] = c
         ks[i, :, : s.shape[-1]] = s
         km[i] = m
-    return dict(q_int8=qi, q_scale=qs, k_int8=ki, k_scale=ks, k_mean=km)
+    out = dict(q_int8=qi, q_scale=qs, k_int8=ki, k_scale=ks, k_mean=km)
+    if smooth_q:
+        out["q_mean"] = qm
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -296,15 +357,18 @@ def qk_int(q_int8: np.ndarray, k_int8: np.ndarray) -> np.ndarray:
 def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndarray,
                         k_scale: np.ndarray, v: np.ndarray, rows: Sequence[int], causal: bool,
                         pv_mode: str = "fp16", v_scale: Optional[np.ndarray] = None,
-                        tile: int = KV_TILE) -> np.ndarray:
+                        tile: int = KV_TILE, score_bias: Optional[np.ndarray] = None) -> np.ndarray:
     """Output rows of the quantised attention for one (sequence, head).
 
     Inputs: q_int8/k_int8 [n, d] codes, q_scale [ceil(n/128)] (softmax scale
     folded in), k_scale [ceil(n/64)]; v fp16 [n, d] (fp16 mode) or e4m3 codes
     [n, d] with v_scale [d] (fp8 mode).  ``rows``: query indices.
+    ``score_bias``: with a smoothed Q, the [ceil(n/128), n] term of
+    ``q_smooth_bias``, added to every score of a row of that Q block.
 
     Steps:
-      * S = int(Q̂K̂ᵀ) · δQ · δK  ([PS] quantisation step 3, C ≈ (ÂB̂)(δAδB));
+      * S = int(Q̂K̂ᵀ) · δQ · δK  ([PS] quantisation step 3, C ≈ (ÂB̂)(δAδB)),
+        plus the Q-smoothing term when given;
       * causal: key j > query i is masked ([CS]: is_causal=True);
       * online softmax over 64-key tiles in ascending order ([IP] §3.1):
         m' = max(m, max_j s), α = e^(m-m'), p = e^(s-m'), l = αl + Σp;
@@ -340,6 +404,8 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
             acc = qf @ k_int8[keys].astype(np.float64).T
             dk = k_scale[keys // K_BLOCK].astype(np.float64)
             s = acc * dq[:, None] * dk[None, :]
+            if score_bias is not None:
+                s = s + score_bias[rows // Q_BLOCK][:, keys]
             if causal:
                 s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
             m_new = np.maximum(m, s.max(axis=1))
@@ -364,20 +430,23 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
 
 
 def score_lse_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndarray, k_scale: np.ndarray,
-                   rows: Sequence[int], causal: bool) -> np.ndarray:
+                   rows: Sequence[int], causal: bool, score_bias: Optional[np.ndarray] = None) -> np.ndarray:
     """Natural-log sum of exp of each row's dequantised scores over its visible
     keys, the quantity that merges partial softmax results over key ranges
     ([IP] §3.1 online softmax keeps it as (m, l): lse = m + log l):
 
-        lse_i = log Σ_{j visible} exp(δQ_i · δK_j · (q̂_i · k̂_j)).
+        lse_i = log Σ_{j visible} exp(δQ_i · δK_j · (q̂_i · k̂_j) [+ bias]).
 
-    Plain definition in fp64 (shifted by the row max before exp).  Returns
-    fp64 [len(rows)]."""
+    ``score_bias`` as for ``sage_attention_rows`` (smoothed Q).  Plain
+    definition in fp64 (shifted by the row max before exp).  Returns fp64
+    [len(rows)]."""
     rows = np.asarray(rows, dtype=np.int64)
     n = k_int8.shape[0]
     keys = np.arange(n)
     acc = q_int8[rows].astype(np.float64) @ k_int8.astype(np.float64).T
     s = acc * q_scale[rows // Q_BLOCK].astype(np.float64)[:, None] * k_scale[keys // K_BLOCK].astype(np.float64)[None, :]
+    if score_bias is not None:
+        s = s + score_bias[rows // Q_BLOCK]
     if causal:
         s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
     mx = s.max(axis=1)

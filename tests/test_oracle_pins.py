@@ -406,3 +406,195 @@ def test_workload_recipe_shapes():
     wv = workloads.get("varlen")
     lens = workloads.sequence_lengths(wv)
     assert len(lens) == 16 and lens.min() >= 512 and lens.max() <= 8192
+
+
+# --------------------------------------------------------------------------
+# Q smoothing
+# --------------------------------------------------------------------------
+def _run_smooth(q, k, v, causal, pv_mode="fp16", rows=None):
+    """The method with Q smoothing for one (sequence, head)."""
+    quant = O.quant_qk_dense(q[None, None], k[None, None], smooth_q=True)
+    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+    bias = O.q_smooth_bias(quant["q_mean"][0, 0], k, quant["k_mean"][0, 0], O.default_sm_scale(q.shape[-1]))
+    rows = np.arange(q.shape[0]) if rows is None else rows
+    if pv_mode == "fp8":
+        vc, vs = O.quant_v_fp8(v)
+        return O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs, score_bias=bias)
+    return O.sage_attention_rows(qi, qs, ki, ks, v, rows, causal, "fp16", score_bias=bias)
+
+
+def test_q_block_mean_exact_rational():
+    """Each 128-token block (the last one partial) gets its own exact mean."""
+    rng = np.random.default_rng(51)
+    for n in (1, 127, 128, 129, 300):
+        q = (rng.standard_normal((n, 5)) * rng.choice([1e-3, 1.0, 300.0]) + 7.0).astype(np.float16)
+        qm = O.q_block_mean(q)
+        assert qm.shape == (-(-n // 128), 5) and qm.dtype == np.float32
+        for b in range(qm.shape[0]):
+            blk = q[128 * b:min(n, 128 * b + 128)]
+            for c in range(5):
+                exact = sum(Fraction(float(v)) for v in blk[:, c]) / len(blk)
+                assert qm[b, c] == fraction_to_f32(exact), (n, b, c)
+
+
+def test_q_smooth_codes_brute_force_and_reconstruction():
+    """Residual codes are the nearest integers (ties to even) to fp32(x/δ) for
+    x = fp32(q) - q̄, and q̄ + δ·q̂ reconstructs q within half a step."""
+    rng = np.random.default_rng(52)
+    n, d = 200, 16
+    q = (rng.standard_normal((n, d)) + 4 * rng.standard_normal(d)).astype(np.float16)
+    sm = np.float32(0.25)
+    codes, scale, qm = O.quant_q_smooth(q, sm)
+    assert scale.shape == (2,) and qm.shape == (2, d)
+    for b in range(2):
+        blk = slice(128 * b, min(n, 128 * b + 128))
+        x = q[blk].astype(np.float32) - qm[b]
+        delta = np.float32(np.abs(x).max() / np.float32(127))
+        assert scale[b] == np.float32(delta * sm)
+        assert np.abs(codes[blk]).max() == 127
+        ratio = (x / delta).astype(np.float32).astype(np.float64)
+        cand = np.arange(-127, 128, dtype=np.float64)
+        for i in range(0, x.shape[0], 7):
+            for c in range(d):
+                dist = np.abs(ratio[i, c] - cand)
+                best = cand[dist == dist.min()]
+                want = best[0] if len(best) == 1 else best[best % 2 == 0][0]
+                assert codes[blk][i, c] == want
+        rec = qm[b].astype(np.float64) + codes[blk].astype(np.float64) * float(delta)
+        assert np.abs(rec - q[blk].astype(np.float64)).max() <= float(delta) * (0.5 + 2 ** -20) + 1e-6
+
+
+def test_q_smoothing_removes_block_offsets():
+    """Q = base + c_b with per-block constant rows c_b and zero-mean base
+    blocks (all on an exact fp16 grid): the block mean is exactly c_b and the
+    residual codes and scales are those of base quantised without smoothing."""
+    rng = np.random.default_rng(53)
+    n, d = 256, 32
+    half = rng.integers(-64, 65, (64, d)).astype(np.float64) / 16.0
+    half[0, 0] = 4.0
+    base_blk = np.concatenate([half, -half])            # every column sums to zero
+    base = np.concatenate([base_blk, base_blk[::-1]])
+    c = rng.integers(-96, 97, (2, d)).astype(np.float64) / 16.0
+    q = base + np.repeat(c, 128, axis=0)
+    q16, base16 = q.astype(np.float16), base.astype(np.float16)
+    assert (q16.astype(np.float64) == q).all() and (base16.astype(np.float64) == base).all()
+    codes, scale, qm = O.quant_q_smooth(q16, np.float32(1.0))
+    assert (qm.astype(np.float64) == c).all()
+    plain_codes, plain_scale = O.quant_q(base16, np.float32(1.0))
+    assert (codes == plain_codes).all() and (scale == plain_scale).all()
+    # the score term the smoothing removed is exactly sm · c_b · x_j
+    k = rng.standard_normal((n, d)).astype(np.float16)
+    km = O.k_token_mean(k)
+    bias = O.q_smooth_bias(qm, k, km, 0.5)
+    x = k.astype(np.float32) - km
+    for b in range(2):
+        for j in (0, 17, 255):
+            want = 0.5 * sum(Fraction(float(c[b, ch])) * Fraction(float(x[j, ch])) for ch in range(d))
+            assert abs(bias[b, j] - float(want)) <= 1e-15 * max(1.0, abs(float(want)))
+
+
+def test_q_smooth_bias_brute_force():
+    """bias[b, j] = sm · Σ_c q̄[b,c]·(fp32(k[j,c]) - km[c]) against exact rationals."""
+    rng = np.random.default_rng(54)
+    n, d = 150, 8
+    q = (rng.standard_normal((n, d)) + 2).astype(np.float16)
+    k = (rng.standard_normal((n, d)) - 1).astype(np.float16)
+    qm = O.q_block_mean(q)
+    km = O.k_token_mean(k)
+    sm = 0.3535533905932738
+    bias = O.q_smooth_bias(qm, k, km, sm)
+    assert bias.shape == (2, n)
+    for b in range(2):
+        for j in range(0, n, 11):
+            terms = []
+            for c in range(d):
+                xjc = np.float32(np.float32(k[j, c]) - km[c])
+                terms.append(Fraction(float(qm[b, c])) * Fraction(float(xjc)))
+            want = Fraction(sm) * sum(terms)
+            scale = float(Fraction(sm) * sum(abs(t) for t in terms))
+            assert abs(bias[b, j] - float(want)) <= 1e-14 * max(scale, 1e-300), (b, j)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_smooth_constant_blocks_give_exact_attention(causal):
+    """Every query of a block equal to one vector c_b (different per block):
+    the residual is zero (scale 0, codes 0), every score is the Q-smoothing
+    term alone, and the method is exact attention up to fp16 P."""
+    rng = np.random.default_rng(55)
+    n, d = 320, 64
+    c = rng.standard_normal((3, d)) * 2
+    q = np.repeat(c, 128, axis=0)[:n].astype(np.float16)
+    k = (rng.standard_normal((n, d)) + 3 * rng.standard_normal(d)).astype(np.float16)
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    quant = O.quant_qk_dense(q[None, None], k[None, None], smooth_q=True)
+    assert (quant["q_scale"] == 0).all() and (quant["q_int8"] == 0).all()
+    ours = _run_smooth(q, k, v, causal)
+    ref = O.sdpa_fp64_rows(q, k, v, np.arange(n), causal)
+    assert cos(ours, ref) >= 0.99999
+    assert np.abs(ours - ref).max() < 4e-3
+    # without the smoothing term every score would be 0 (plain mean of V)
+    quant0 = O.quant_qk_dense(q[None, None], k[None, None], smooth_q=True)
+    qi, qs, ki, ks = O.head_views_dense(quant0, 0, 0)
+    flat = O.sage_attention_rows(qi, qs, ki, ks, v, np.arange(n), causal)
+    assert cos(flat, ref) < 0.99
+
+
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+def test_q_smoothing_improves_biased_q(pv_mode):
+    """With a token-shared Q bias, Q smoothing brings the method closer to
+    exact attention than K smoothing alone."""
+    x = workloads.generate_custom(56, 1, 2, 700, 128, k_bias=3.0, q_bias=3.0)
+    for h in range(2):
+        q, k, v = x.q[0, h], x.k[0, h], x.v[0, h]
+        ref = O.sdpa_fp64_rows(q, k, v, np.arange(700), False)
+        plain = cos(_run(q, k, v, False, pv_mode), ref)
+        smooth = cos(_run_smooth(q, k, v, False, pv_mode), ref)
+        assert smooth > plain
+        assert smooth >= (0.9999 if pv_mode == "fp16" else 0.9995)
+
+
+def test_q_smooth_lse_pins():
+    """LSE with the smoothing term: scipy's logsumexp over independently formed
+    scores, and for constant Q blocks the LSE of exact scaled scores."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(57)
+    n, d = 200, 64
+    q = (rng.standard_normal((n, d)) + 2 * rng.standard_normal(d)).astype(np.float16)
+    k = (rng.standard_normal((n, d)) + 3 * rng.standard_normal(d)).astype(np.float16)
+    quant = O.quant_qk_dense(q[None, None], k[None, None], smooth_q=True)
+    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+    sm = O.default_sm_scale(d)
+    bias = O.q_smooth_bias(quant["q_mean"][0, 0], k, quant["k_mean"][0, 0], sm)
+    rows = np.array([0, 5, 127, 128, 199])
+    for causal in (False, True):
+        got = O.score_lse_rows(qi, qs, ki, ks, rows, causal, score_bias=bias)
+        for r, i in enumerate(rows):
+            vis = np.arange(i + 1) if causal else np.arange(n)
+            s = [float(qs[i // 128]) * float(ks[j // 64]) * sum(int(a) * int(b) for a, b in zip(qi[i], ki[j]))
+                 + bias[i // 128, j] for j in vis]
+            assert abs(got[r] - logsumexp(s)) <= 1e-12 * max(1.0, abs(got[r]))
+    # constant blocks: lse = logsumexp of sm · q · (k - km), exactly the
+    # plain scores up to the row constant sm · q · km
+    c = rng.standard_normal((2, d))
+    qc = np.repeat(c, 128, axis=0)[:n].astype(np.float16)
+    quant = O.quant_qk_dense(qc[None, None], k[None, None], smooth_q=True)
+    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+    bias = O.q_smooth_bias(quant["q_mean"][0, 0], k, quant["k_mean"][0, 0], sm)
+    got = O.score_lse_rows(qi, qs, ki, ks, rows, False, score_bias=bias)
+    kf = k.astype(np.float64) - quant["k_mean"][0, 0].astype(np.float64)
+    want = logsumexp((qc[rows].astype(np.float64) @ kf.T) * float(sm), axis=1)
+    assert np.abs(got - want).max() <= 1e-5
+
+
+def test_q_smooth_varlen_equals_per_sequence_dense():
+    x = workloads.generate_custom(58, 0, 2, 0, 64, lengths=[1, 130, 300], q_bias=2.0)
+    cu = x.cu_seqlens
+    quant = O.quant_qk_varlen(x.q, x.k, cu, smooth_q=True)
+    for i in range(3):
+        a, b = cu[i], cu[i + 1]
+        dense = O.quant_qk_dense(x.q[:, a:b][None], x.k[:, a:b][None], smooth_q=True)
+        nq = dense["q_scale"].shape[-1]
+        assert (quant["q_int8"][:, a:b] == dense["q_int8"][0]).all()
+        assert (quant["q_scale"][i, :, :nq] == dense["q_scale"][0]).all()
+        assert (quant["q_mean"][i, :, :nq] == dense["q_mean"][0]).all()
+        assert np.isnan(quant["q_mean"][i, :, nq:]).all()
