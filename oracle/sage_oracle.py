@@ -357,7 +357,8 @@ def qk_int(q_int8: np.ndarray, k_int8: np.ndarray) -> np.ndarray:
 def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndarray,
                         k_scale: np.ndarray, v: np.ndarray, rows: Sequence[int], causal: bool,
                         pv_mode: str = "fp16", v_scale: Optional[np.ndarray] = None,
-                        tile: int = KV_TILE, score_bias: Optional[np.ndarray] = None) -> np.ndarray:
+                        tile: int = KV_TILE, score_bias: Optional[np.ndarray] = None,
+                        score_eps: Optional[np.ndarray] = None):
     """Output rows of the quantised attention for one (sequence, head).
 
     Inputs: q_int8/k_int8 [n, d] codes, q_scale [ceil(n/128)] (softmax scale
@@ -365,6 +366,13 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
     [n, d] with v_scale [d] (fp8 mode).  ``rows``: query indices.
     ``score_bias``: with a smoothed Q, the [ceil(n/128), n] term of
     ``q_smooth_bias``, added to every score of a row of that Q block.
+    ``score_eps`` (fp8 mode): a [ceil(n/128), n] bound on how far another
+    correct evaluation may move each score (natural-log units).  Every P code
+    whose 448·p could then round to a neighbouring e4m3 value is a code the
+    method leaves open; the function also returns, per output element, the
+    largest change such a choice of codes, together with the ε-size change
+    of the row sum, can make (fp64 [len(rows), d]), so that a comparison can
+    accept exactly those outputs.
 
     Steps:
       * S = int(Q̂K̂ᵀ) · δQ · δK  ([PS] quantisation step 3, C ≈ (ÂB̂)(δAδB)),
@@ -395,6 +403,8 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     O = np.zeros((R, d))
+    W = np.zeros((R, d))       # bound on |O - O'| over the open P codes (fp8 with score_eps)
+    Wabs = np.zeros((R, d))    # the same sum of P̂·V̂ in absolute values
     last_row = int(rows.max()) if R else -1
     with np.errstate(invalid="ignore", over="ignore"):
         for t0 in range(0, n, tile):
@@ -421,11 +431,28 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
                 pq = e4m3_decode(e4m3_encode(p * E4M3_MAX))
                 A = pq @ vv[keys]                       # level 1: this tile only
                 O = alpha[:, None] * O + A              # level 2: running output
+                if score_eps is not None:
+                    # p moves by at most a factor e^(±2ε): ε from the score and ε
+                    # from the tile max it is taken against; e4m3 rounding is
+                    # monotone, so the code stays between those of the ends
+                    e2 = 2.0 * score_eps[rows // Q_BLOCK][:, keys]
+                    lo = e4m3_decode(e4m3_encode(p * E4M3_MAX * np.exp(-e2)))
+                    hi = e4m3_decode(e4m3_encode(np.minimum(p * E4M3_MAX * np.exp(e2), E4M3_MAX)))
+                    dcode = np.maximum(np.abs(hi - pq), np.abs(pq - lo))
+                    W = alpha[:, None] * W + dcode @ np.abs(vv[keys])
+                    Wabs = alpha[:, None] * Wabs + pq @ np.abs(vv[keys])
             m = m_new
     if pv_mode == "fp16":
         out = O / l[:, None]
     else:
         out = O * v_scale.astype(np.float64)[None, :] / (E4M3_MAX * l[:, None])
+        if score_eps is not None:
+            # each tile's share is weighted by e^(m_t - m_final) and the row
+            # sum by e^(±2ε) as well: with γ = e^(4ε) - 1 over the row,
+            # |out' - out| <= (W + γ·(W + 2·Wabs))·δV / (448·l)
+            gamma = np.expm1(4.0 * score_eps[rows // Q_BLOCK].max(axis=1))[:, None]
+            bound = (W + gamma * (W + 2.0 * Wabs)) * v_scale.astype(np.float64)[None, :] / (E4M3_MAX * l[:, None])
+            return out.astype(np.float16), bound
     return out.astype(np.float16)
 
 

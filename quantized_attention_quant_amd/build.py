@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libsage.so")
 
-SOURCES = ["api.cpp", "quant.hip", "attn.hip"]
+SOURCES = ["api.cpp", "quant.hip", "smooth_q.hip", "attn.hip"]
 HEADERS = ["sage_common.h", "sage_internal.h"]
 
 ARCH = "gfx950"

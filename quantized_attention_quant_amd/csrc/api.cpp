@@ -29,18 +29,23 @@ inline bool debug_sync() {
 
 // Offsets inside the attention workspace:
 // [0] q_int8 [1] k_int8 [2] q_scale [3] k_scale [4] k_mean [5] packed V
-// [6] v_scale (fp8) [7] int64 K column sums; total returned separately.
+// [6] v_scale (fp8) [7] int64 K column sums; with a smoothed Q [8] q_mean,
+// [9] accumulator initial values, [10] fp32 fallback terms, [11] fallback
+// flags; total returned separately.
+constexpr int kWsRegions = 12;
 struct WsLayout {
-  size_t off[8];
+  size_t off[kWsRegions];
   size_t total;
 };
 
-WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d, bool fp8) {
+WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d, bool fp8, bool smooth_q) {
   const int64_t tokens = varlen ? (int64_t)H * T : (int64_t)B * H * N;
   const int64_t ktokens = varlen ? (int64_t)Hkv * T : (int64_t)B * Hkv * N;
   const int64_t nqb = ceil_div64(N, sage::kQBlock), nkb = ceil_div64(N, sage::kKBlock);
   const int64_t vtiles = varlen ? (int64_t)Hkv * sage::vtiles_per_head_varlen(T, B) : (int64_t)B * Hkv * nkb;
-  const size_t sizes[8] = {
+  const size_t qblocks = (size_t)B * H * nqb;  // (sequence, head, Q block) rows
+  const size_t sq = smooth_q ? 1 : 0;
+  const size_t sizes[kWsRegions] = {
       (size_t)(tokens * d),
       (size_t)(ktokens * d),
       sizeof(float) * (size_t)B * H * nqb,
@@ -49,10 +54,14 @@ WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d
       (size_t)vtiles * sage::kKBlock * d * (fp8 ? 1 : 2),
       fp8 ? sizeof(float) * (size_t)B * Hkv * d : 0,
       sizeof(long long) * (size_t)B * Hkv * d,
+      sq * sizeof(float) * qblocks * d,
+      sq * sizeof(int32_t) * qblocks * (size_t)(nkb * sage::kKBlock),
+      sq * sizeof(float) * qblocks * (size_t)(nkb * sage::kKBlock),
+      sq * sizeof(int32_t) * qblocks * (size_t)(2 * nkb),
   };
   WsLayout L;
   size_t cur = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kWsRegions; ++i) {
     L.off[i] = cur;
     cur = align_up(cur + sizes[i]);
   }
@@ -98,8 +107,8 @@ sage_status_t finish(hipStream_t st) {
 // Shared body of the dense and varlen forward.  g: geometry of Q and O; K and V
 // have Hkv heads over the same sequences.
 sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o, float* lse, const SeqGeom& g,
-                           int Hkv, bool varlen, int is_causal, sage_pv_mode_t pv_mode, float sm_scale,
-                           void* workspace, size_t workspace_bytes, sage_stream_t stream) noexcept {
+                           int Hkv, bool varlen, int is_causal, sage_pv_mode_t pv_mode, int smooth_q,
+                           float sm_scale, void* workspace, size_t workspace_bytes, sage_stream_t stream) noexcept {
   if (!q || !k || !v || !o || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
   if (!kv_heads_ok(g.H, Hkv)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -109,7 +118,8 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   float sm;
   if (!resolve_sm_scale(sm_scale, g.d, &sm)) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
-  const WsLayout L = make_layout(varlen, g.B, g.H, Hkv, g.N, g.T, g.d, fp8);
+  const bool sq = smooth_q != 0;
+  const WsLayout L = make_layout(varlen, g.B, g.H, Hkv, g.N, g.T, g.d, fp8, sq);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const int64_t rows = varlen ? (int64_t)g.H * g.T : (int64_t)g.B * g.H * g.N;
   const size_t tensor_bytes = (size_t)rows * g.d * 2;
@@ -134,13 +144,27 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   uint8_t* vp = reinterpret_cast<uint8_t*>(ws + L.off[5]);
   float* vs = reinterpret_cast<float*>(ws + L.off[6]);
   long long* colsum = reinterpret_cast<long long*>(ws + L.off[7]);
+  float* qm = sq ? reinterpret_cast<float*>(ws + L.off[8]) : nullptr;
+  int32_t* slots = reinterpret_cast<int32_t*>(ws + L.off[9]);
+  float* fix = reinterpret_cast<float*>(ws + L.off[10]);
+  int32_t* flags = reinterpret_cast<int32_t*>(ws + L.off[11]);
 
   SeqGeom gk = g;
   gk.H = Hkv;
-  sage::launch_quant_qk(g, gk, q, k, sm, q8, k8, qs, ks, km, colsum, st);
+  sage::launch_quant_qk(g, gk, q, k, sm, q8, k8, qs, ks, km, qm, colsum, st);
+  if (sq) {
+    const sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, ks, qm, qs, slots, fix, flags, g, g.H / Hkv,
+                             (float)((double)sm * 1.4426950408889634), is_causal != 0};
+    sage::launch_q_bias(qa, st);
+  }
   if (fp8) sage::launch_v_scale(gk, v, vs, st);
   sage::launch_v_prepare(gk, v, vs, fp8, /*rowmajor=*/false, vp, st);
   sage::AttnArgs a{q8, k8, qs, ks, vp, vs, static_cast<uint16_t*>(o), lse, g, g.H / Hkv};
+  if (sq) {
+    a.qb_slots = slots;
+    a.qb_fix = fix;
+    a.qb_flags = flags;
+  }
   sage::launch_attn(a, is_causal != 0, fp8, st);
   return finish(st);
 }
@@ -179,8 +203,8 @@ size_t sage_quant_qk_workspace_size(int B, int H, int d) {
 
 sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, sage_layout_t layout,
                             const int32_t* cu_seqlens, int64_t total_tokens, float sm_scale, int8_t* q_int8,
-                            int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, void* workspace,
-                            size_t workspace_bytes, sage_stream_t stream) {
+                            int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, float* q_mean,
+                            void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
   SeqGeom g;
   if (cu_seqlens) {
@@ -194,14 +218,15 @@ sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, i
   if (!q || !k || !q_int8 || !k_int8 || !q_scale || !k_scale || !k_mean || !workspace)
     return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_int8) || !aligned16(k_int8) || !aligned16(q_scale) ||
-      !aligned16(k_scale) || !aligned16(k_mean) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
+      !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(q_mean) ||
+      (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
     return SAGE_ERR_INVALID_ARGUMENT;
   float sm;
   if (!resolve_sm_scale(sm_scale, d, &sm)) return SAGE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < sage_quant_qk_workspace_size(g.B, H, d)) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   if (cu_seqlens && total_tokens == 0) return SAGE_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  sage::launch_quant_qk(g, g, q, k, sm, q_int8, k_int8, q_scale, k_scale, k_mean,
+  sage::launch_quant_qk(g, g, q, k, sm, q_int8, k_int8, q_scale, k_scale, k_mean, q_mean,
                         static_cast<long long*>(workspace), st);
   return finish(st);
 }
@@ -228,57 +253,61 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
   return finish(st);
 }
 
-size_t sage_attn_workspace_size(int B, int H, int H_kv, int N, int d, sage_pv_mode_t pv_mode) {
+size_t sage_attn_workspace_size(int B, int H, int H_kv, int N, int d, sage_pv_mode_t pv_mode, int smooth_q) {
   if (check_dims(B, H, N, d) != SAGE_OK || !kv_heads_ok(H, H_kv)) return 0;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
-  return make_layout(false, B, H, H_kv, N, 0, d, pv_mode == SAGE_PV_FP8_E4M3).total;
+  return make_layout(false, B, H, H_kv, N, 0, d, pv_mode == SAGE_PV_FP8_E4M3, smooth_q != 0).total;
 }
 
 sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                             int H_kv, int N, int d, sage_layout_t layout, int is_causal, sage_pv_mode_t pv_mode,
-                            float sm_scale, void* workspace, size_t workspace_bytes, sage_stream_t stream) {
+                            int smooth_q, float sm_scale, void* workspace, size_t workspace_bytes,
+                            sage_stream_t stream) {
   if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
   const sage_status_t s = check_dims(B, H, N, d);
   if (s != SAGE_OK) return s;
   const SeqGeom g{nullptr, B, H, N, d, 0};
-  return attn_forward(q, k, v, o, lse, g, H_kv, false, is_causal, pv_mode, sm_scale, workspace, workspace_bytes,
-                      stream);
+  return attn_forward(q, k, v, o, lse, g, H_kv, false, is_causal, pv_mode, smooth_q, sm_scale, workspace,
+                      workspace_bytes, stream);
 }
 
 size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H, int H_kv, int d,
-                                       sage_pv_mode_t pv_mode) {
+                                       sage_pv_mode_t pv_mode, int smooth_q) {
   if (nseq < 1 || total_tokens < 0 || check_dims(nseq, H, max_seqlen, d) != SAGE_OK || !kv_heads_ok(H, H_kv))
     return 0;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
-  return make_layout(true, nseq, H, H_kv, max_seqlen, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3).total;
+  return make_layout(true, nseq, H, H_kv, max_seqlen, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3, smooth_q != 0)
+      .total;
 }
 
 sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                    const int32_t* cu_seqlens, int nseq, int max_seqlen, int64_t total_tokens, int H,
-                                   int H_kv, int d, int is_causal, sage_pv_mode_t pv_mode, float sm_scale,
-                                   void* workspace, size_t workspace_bytes, sage_stream_t stream) {
+                                   int H_kv, int d, int is_causal, sage_pv_mode_t pv_mode, int smooth_q,
+                                   float sm_scale, void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   SeqGeom g;
   const sage_status_t s = varlen_geom(cu_seqlens, nseq, max_seqlen, total_tokens, H, d, &g);
   if (s != SAGE_OK) return s;
-  return attn_forward(q, k, v, o, lse, g, H_kv, true, is_causal, pv_mode, sm_scale, workspace, workspace_bytes,
-                      stream);
+  return attn_forward(q, k, v, o, lse, g, H_kv, true, is_causal, pv_mode, smooth_q, sm_scale, workspace,
+                      workspace_bytes, stream);
 }
 
 sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int N, int64_t total_tokens, int d,
-                                         sage_pv_mode_t pv_mode, size_t offsets_out[8]) {
+                                         sage_pv_mode_t pv_mode, int smooth_q, size_t offsets_out[12]) {
   if (!offsets_out) return SAGE_ERR_INVALID_ARGUMENT;
   if (check_dims(B, H, N, d) != SAGE_OK || !kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
   if (varlen && total_tokens < 0) return SAGE_ERR_INVALID_ARGUMENT;
-  const WsLayout L = make_layout(varlen != 0, B, H, H_kv, N, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3);
+  const WsLayout L =
+      make_layout(varlen != 0, B, H, H_kv, N, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3, smooth_q != 0);
   for (int i = 0; i < 7; ++i) offsets_out[i] = L.off[i];
-  offsets_out[7] = L.total;
+  for (int i = 8; i < kWsRegions; ++i) offsets_out[i - 1] = L.off[i];
+  offsets_out[11] = L.total;
   return SAGE_OK;
 }
 
 sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int N, int d, int is_causal,
-                                            sage_pv_mode_t pv_mode, const void* workspace, size_t workspace_bytes,
-                                            sage_stream_t stream) {
+                                            sage_pv_mode_t pv_mode, int smooth_q, const void* workspace,
+                                            size_t workspace_bytes, sage_stream_t stream) {
   const sage_status_t s = check_dims(B, H, N, d);
   if (s != SAGE_OK) return s;
   if (!kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -286,7 +315,7 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
     return SAGE_ERR_INVALID_ARGUMENT;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
-  const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, fp8);
+  const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, fp8, smooth_q != 0);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const size_t tensor_bytes = (size_t)B * H * N * d * 2;
   if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -296,6 +325,11 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
                    reinterpret_cast<const float*>(ws + L.off[2]), reinterpret_cast<const float*>(ws + L.off[3]),
                    reinterpret_cast<const uint8_t*>(ws + L.off[5]), reinterpret_cast<const float*>(ws + L.off[6]),
                    static_cast<uint16_t*>(o), nullptr, g, H / H_kv};
+  if (smooth_q) {
+    a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[9]);
+    a.qb_fix = reinterpret_cast<const float*>(ws + L.off[10]);
+    a.qb_flags = reinterpret_cast<const int32_t*>(ws + L.off[11]);
+  }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   sage::launch_attn(a, is_causal != 0, fp8, st);
   return finish(st);

@@ -38,6 +38,12 @@
 //   * Workgroup ids are remapped so that one XCD runs consecutive query blocks
 //     of the same head (K̂/V reuse in that XCD's L2); heavier causal blocks go
 //     first.
+//   * Smoothed Q (dtcms summary, "SageAttention 2"; smooth_q.hip forms the
+//     term): the part of each score that Q's block mean carries enters as the
+//     accumulator's initial value — magic bias plus that term in units of the
+//     tile's δQ·δK, streamed into LDS with the tile — so the softmax does no
+//     extra work; half tiles whose term does not fit that integer range add it
+//     in fp32 instead (rare: a flag per half tile).
 #include "sage_common.h"
 #include "sage_internal.h"
 
@@ -48,24 +54,37 @@ constexpr int kMagicI = 0x4B400000;     // its fp32 bit pattern
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2E4M3Max = 8.807354922057604f;  // log2(448)
 // FP16 PV: the exponent reference is only moved when a lane's row-tile sum of
-// p exceeds 2^kLazyRescale, so p <= 2^8 and the output rescale is rare.
-constexpr float kLazyRescale = 8.0f;
-constexpr float kLazyLimit = 256.0f;  // 2^kLazyRescale
-constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
-constexpr int kStages = 3;
+// p exceeds kLazyLimit = 2^8, so p <= 2^8 and the output rescale is rare.
+constexpr float kLazyLimit = 256.0f;
+[[maybe_unused]] constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit data format
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-template <int D, bool FP8, int NT = kThreads>
+// One LDS stage: K̂ tile, packed V tile and, with a smoothed Q, the
+// accumulator initial values of the tile's 64 keys for the workgroup's two Q
+// blocks (four 256-byte quarters: quarter w holds block w/2, keys 32(w%2) ..
+// +31 in its first 128 bytes).
+template <int D, bool FP8, int NT = kThreads, bool SM = false>
 struct TileGeom {
   static constexpr int KBYTES = kKBlock * D;                    // K̂ tile, int8
   static constexpr int VBYTES = kKBlock * D * (FP8 ? 1 : 2);    // packed V tile
+  static constexpr int SBYTES = SM ? 1024 : 0;                  // accumulator initial values
   static constexpr int KCHUNKS = KBYTES / 16;
   static constexpr int VCHUNKS = VBYTES / 16;
   static constexpr int KI = KCHUNKS / NT;                       // DMA instructions per wave
   static constexpr int VI = VCHUNKS / NT;
-  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int SI = SM ? 1 : 0;
+  static constexpr int STAGE = KBYTES + VBYTES + SBYTES;
   static_assert(KI * NT == KCHUNKS && VI * NT == VCHUNKS, "tile must split evenly over the waves");
+};
+
+// Where a tile's accumulator initial values come from (smoothed Q only): the
+// workgroup's first Q block's row of int32 values, `bytes` long (one or two
+// rows of npad keys).
+struct SlotSrc {
+  const int32_t* base;
+  int bytes;
+  int npad;
 };
 
 // 16-byte chunk index of K̂ tile row r, chunk c inside LDS (XOR swizzle).  A
@@ -90,11 +109,11 @@ __device__ __forceinline__ int k_lds_chunk(int r, int c) {
 // the head-sequence's K̂ rows and packed V tiles; reads past them return zero.
 // Lane i of a DMA instruction lands at the instruction's LDS base + 16·i, so
 // each lane fetches the global chunk that belongs at its swizzled position.
-template <int D, bool FP8, int NT = kThreads>
+template <int D, bool FP8, int NT = kThreads, bool SM = false>
 __device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const void* vbase, int vbytes, int t,
-                                           char* stage, int w, int lane) {
+                                           char* stage, int w, int lane, const SlotSrc& ss = SlotSrc{}) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the buffer-descriptor type exists only for the GPU target
-  using G = TileGeom<D, FP8, NT>;
+  using G = TileGeom<D, FP8, NT, SM>;
   constexpr int CPR = D / 16;
   const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), (short)0, kbytes,
                                                                       kBufferFlags);
@@ -114,6 +133,15 @@ __device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const 
     const int base = (w * G::VI + j) * 64;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + base * 16), 16,
                                              t * G::VBYTES + (base + lane) * 16, 0, 0, 0);
+  }
+  if (SM) {
+    // quarter w (w < 4): lanes 0-31 fetch block w/2, keys 64t + 32(w%2) + lane;
+    // lanes 32-63 read past the range (zeros) into the quarter's unused half
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(ss.base), (short)0,
+                                                                        ss.bytes, kBufferFlags);
+    const int off = lane < 32 ? ((w >> 1) * ss.npad + t * kKBlock + 32 * (w & 1) + lane) * 4 : ss.bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(stage + G::KBYTES + G::VBYTES + w * 256), 4, off, 0,
+                                             0, 0);
   }
 #endif
 }
@@ -149,6 +177,10 @@ __device__ __forceinline__ void wait_dma_and_sync() {
 __device__ __forceinline__ float load_uniform(const float* p, int64_t i) {
   return ((const __attribute__((address_space(4))) float*)p)[i];
 }
+typedef int v2i __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ v2i load_uniform2(const int32_t* p, int64_t i) {  // i even
+  return ((const __attribute__((address_space(4))) v2i*)p)[i / 2];
+}
 
 // max / sum over the two lanes that hold the same query row (l and l ^ 32).
 __device__ __forceinline__ float pair_max(float x) {
@@ -183,14 +215,25 @@ __device__ __forceinline__ void load_k_frags(const v4i* __restrict__ lds_k, v4i 
 
 // Sᵀ of one 32-query half for one 64-key tile: S[s] covers keys 32s..32s+31;
 // lane (r32, g) reg i holds key 32s + 8(i/4) + 4g + i%4 of query r32, as
-// magic + Σ q̂·k̂.
-template <int D>
-__device__ __forceinline__ void qk_half(const v4i (&kf)[2][D / 32], const v4i (&qf)[D / 32], v16i (&S)[2]) {
+// magic + Σ q̂·k̂ — or, with a smoothed Q (SM), as the initial value of that
+// key (lslots: the wave's Q block's 64 values in LDS) + Σ q̂·k̂.
+template <int D, bool SM = false>
+__device__ __forceinline__ void qk_half(const v4i (&kf)[2][D / 32], const v4i (&qf)[D / 32], v16i (&S)[2],
+                                        const v4i* __restrict__ lslots = nullptr, int g = 0) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     v16i acc;
+    if (SM) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = kMagicI;
+      for (int q = 0; q < 4; ++q) {
+        const v4i init = lslots[16 * s + 2 * q + g];  // keys 32s + 8q + 4g .. +3
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * q + j] = init[j];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = kMagicI;
+    }
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[s][ks], qf[ks], acc, 0, 0, 0);
     S[s] = acc;
@@ -222,13 +265,15 @@ __device__ __forceinline__ float tile_max(float mx, float c2) {
   return (mx == 0.f) ? -__builtin_inff() : (mx - kMagicF) * c2;
 }
 
-// FP16 PV: p = 2^(F·c - K), K = fl(1.5·2^23·c + m_ref) — one FMA per score.
-// The rounding of K shifts a row-tile's exponents by <= ulp(K)/2, a common
-// factor on its p and on its share of l.  P is packed as four B operands; the
-// returned row-tile sum is over the unrounded p, in fp32 adds (dot instructions
-// would share the matrix pipeline and stall behind the other wave's MFMAs).
-__device__ __forceinline__ float exp_pack_fp16(const float (&F)[2][16], float c2, float m_ref, v8h (&pk)[4]) {
-  const float kb = __builtin_fmaf(kMagicF, c2, m_ref);
+// FP16 PV: p = 2^(F·c - K), K = fl(M·c + m_ref) — one FMA per score, M the
+// bias of F (1.5·2^23, or 0 for scores already in log2 units).  The rounding
+// of K shifts a row-tile's exponents by <= ulp(K)/2, a common factor on its p
+// and on its share of l.  P is packed as four B operands; the returned
+// row-tile sum is over the unrounded p, in fp32 adds (dot instructions would
+// share the matrix pipeline and stall behind the other wave's MFMAs).
+__device__ __forceinline__ float exp_pack_fp16(const float (&F)[2][16], float c2, float m_ref, v8h (&pk)[4],
+                                               float M = kMagicF) {
+  const float kb = __builtin_fmaf(M, c2, m_ref);
   float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
@@ -289,12 +334,13 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ vstage, int lan
 // QKᵀ of the current one in one scheduling region.  All K̂ fragment reads go
 // first; then every MFMA is followed by one V fragment read while any remain,
 // so each LDS read has several MFMAs (>= 256 cycles) to land before its use.
-template <int D, bool FP8>
+template <int D, bool FP8, bool SM = false>
 __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, const char* __restrict__ vstage,
                                             int lane, int r32, int gg, const v4i (&qf)[D / 32], v16i (&S)[2],
-                                            const v8h (&pk16)[4], const v8i& pk8, v16f (&O)[D / 32]) {
+                                            const v8h (&pk16)[4], const v8i& pk8, v16f (&O)[D / 32],
+                                            const v4i* __restrict__ lslots = nullptr) {
   constexpr int DT = D / 32;
-  constexpr int NK = 2 * DT;                 // K̂ fragment reads (128-bit)
+  constexpr int NK = 2 * DT + (SM ? 8 : 0);  // K̂ fragment (+ initial value) reads (128-bit)
   constexpr int NV = FP8 ? 2 * DT : 4 * DT;  // V fragment reads (128-bit)
   constexpr int NQK = 2 * DT;                // QKᵀ MFMAs
   constexpr int NPV = FP8 ? DT : 4 * DT;     // PV MFMAs
@@ -305,7 +351,7 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
     v8h vf[4 * DT];
 #pragma unroll
     for (int i = 0; i < 4 * DT; ++i) vf[i] = lv[i * 64 + lane];
-    qk_half<D>(kf, qf, S);
+    qk_half<D, SM>(kf, qf, S, lslots, gg);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
@@ -316,7 +362,7 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
     v8i vf[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[dt] = lv[dt * 64 + lane];
-    qk_half<D>(kf, qf, S);
+    qk_half<D, SM>(kf, qf, S, lslots, gg);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[dt], pk8, O[dt], 0, 0, 0, 0, 0, 0);
@@ -351,10 +397,12 @@ struct WaveCtx {
   float l_run;      // this lane's share of the row sum
 };
 
-// Row max of the tile's scores (magic-biased; 0 when nothing is visible), over
-// both lanes of the row.
+// Row max of the tile's scores over both lanes of the row.  Magic-biased
+// scores are positive, so the neutral value 0 (nothing visible) is enough;
+// with SIGNED scores (log2 units) it is -inf.
+template <bool SIGNED = false>
 __device__ __forceinline__ float row_max(const float (&F)[2][16]) {
-  float mx = 0.f;
+  float mx = SIGNED ? -__builtin_inff() : 0.f;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -367,14 +415,18 @@ __device__ __forceinline__ float row_max(const float (&F)[2][16]) {
 // the output rescale — O is rescaled in one place only.
 //
 // FP16: P is formed against the current reference m first.  If every lane's
-// sum of p stays <= 2^kLazyRescale, no p exceeds that bound and the tile is
+// sum of p stays <= kLazyLimit, no p exceeds that bound and the tile is
 // done without a row max; otherwise (a row max passed m by more than
-// kLazyRescale, or the first visible tile of a row) m moves to the row max,
+// 8 (log2 units), or the first visible tile of a row) m moves to the row max,
 // O and l are rescaled and P is formed again.  Softmax does not depend on the
 // reference and fp16 rounding is relative, so this changes nothing but
 // rounding.  FP8: the codes follow the running max exactly, tile by tile.
-template <int D, bool FP8>
-__device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2) {
+//
+// SM (smoothed Q): F is either magic-biased (M = 1.5·2^23) or, in a tile that
+// took the fp32 path, already the score in log2 units (c2 = 1, M = 0), so the
+// row max starts from -inf and the tile max is (max F - M)·c2.
+template <int D, bool FP8, bool SM = false>
+__device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2, float M = kMagicF) {
   float F[2][16];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -388,19 +440,20 @@ __device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2) {
   if (!FP8) {
     // a row that has seen no visible key keeps m = -inf: its p become +inf
     // (visible) or 0 (masked), and the check below moves m
-    float lsum = exp_pack_fp16(F, c2, __builtin_fmaxf(c.m_run, -3.0e38f), c.pk16);
+    float lsum = exp_pack_fp16(F, c2, __builtin_fmaxf(c.m_run, -3.0e38f), c.pk16, SM ? M : kMagicF);
     if (__any(!(lsum <= kLazyLimit))) {
-      const float mt = tile_max(row_max(F), c2);
+      const float mt = SM ? (row_max<true>(F) - M) * c2 : tile_max(row_max(F), c2);
       float m_new = __builtin_fmaxf(c.m_run, mt);
       m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
       rescale_o<D>(c.O, c.l_run, __builtin_amdgcn_exp2f(c.m_run - m_new));
       c.m_run = m_new;
-      lsum = exp_pack_fp16(F, c2, m_new, c.pk16);
+      lsum = exp_pack_fp16(F, c2, m_new, c.pk16, SM ? M : kMagicF);
     }
     c.l_run += lsum;
   } else {
-    const float mx = row_max(F);
-    const float mt = tile_max(mx, c2);
+    float mx = SM ? row_max<true>(F) : row_max(F);
+    const float mt = SM ? (mx - M) * c2 : tile_max(mx, c2);
+    if (SM) mx = (mx == -__builtin_inff()) ? 0.f : mx;  // all masked: F - 0 = -inf gives p = 0
     float m_new = __builtin_fmaxf(c.m_run, mt);
     m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(c.m_run - m_new);
@@ -435,16 +488,17 @@ __device__ __forceinline__ void wait_tiles(int pending) {
 }
 
 // d=64 fits 128 VGPRs, so two workgroups share a CU (four waves per SIMD) and
-// their independent phases fill each other's stalls; d=128 needs ~180.
-template <int D>
-constexpr int kAttnWavesPerSimd = (D == 64) ? 4 : 2;
+// their independent phases fill each other's stalls; d=128 needs ~180, and so
+// does d=64 with a smoothed Q (its accumulator initial values would spill).
+template <int D, bool SM>
+constexpr int kAttnWavesPerSimd = (D == 64 && !SM) ? 4 : 2;
 
-template <int D, bool FP8, bool CAUSAL>
+template <int D, bool FP8, bool CAUSAL, bool SM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads),
-                          amdgpu_waves_per_eu(kAttnWavesPerSimd<D>, kAttnWavesPerSimd<D>)))
+                          amdgpu_waves_per_eu(kAttnWavesPerSimd<D, SM>, kAttnWavesPerSimd<D, SM>)))
 void attn_fwd_kernel(AttnArgs a) {
   constexpr int DT = D / 32;  // 32-wide d tiles of the output
-  using G = TileGeom<D, FP8, kThreads>;  // tiles are streamed by the 4 waves of group A
+  using G = TileGeom<D, FP8, kThreads, SM>;  // tiles are streamed by the 4 waves of group A
   __shared__ __attribute__((aligned(1024))) char smem[kRingStages * G::STAGE];
 
   const SeqGeom& g = a.g;
@@ -485,7 +539,14 @@ void attn_fwd_kernel(AttnArgs a) {
   const int kbytes = n * D;
   const uint8_t* vbase = a.v_packed + vtile_index(gk, b, hk, 0) * G::VBYTES;
   const int vbytes = ceil_div(n, kKBlock) * G::VBYTES;
-  constexpr int L = G::KI + G::VI;  // DMA instructions per group-A wave per tile
+  constexpr int L = G::KI + G::VI + G::SI;  // DMA instructions per group-A wave per tile
+  // smoothed Q: this workgroup's rows of accumulator initial values (Q blocks
+  // q0/128 and, if it exists, the next), fallback flags and fp32 terms
+  const int npad = nkb * kKBlock;
+  const int wqb = wq_lo / kQBlock;  // this wave's Q block
+  SlotSrc ss{};
+  if (SM) ss = SlotSrc{a.qb_slots + (hs * nqb + q0 / kQBlock) * (int64_t)npad, (q0 + kQBlock < n ? 2 : 1) * npad * 4,
+                       npad};
 
   WaveCtx<D, FP8> c;
   load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
@@ -504,7 +565,7 @@ void attn_fwd_kernel(AttnArgs a) {
   if (lead) {
     const int first = min(kAhead, ntiles);
     for (int t = 0; t < first; ++t)
-      issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, t, smem + t * G::STAGE, w, lane);
+      issue_tile<D, FP8, kThreads, SM>(kbase, kbytes, vbase, vbytes, t, smem + t * G::STAGE, w, lane, ss);
   }
   // the first tiles and this wave's Q̂ fragments have landed; an empty queue
   // here also lets the compiler see that no later MFMA waits on the Q̂ loads
@@ -518,10 +579,39 @@ void attn_fwd_kernel(AttnArgs a) {
       const int k0 = u * kKBlock;
       // c > 0 keeps -inf·c = -inf for masked keys; a zero scale means all
       // scores of the tile are 0, for which the smallest normal gives the same
-      const float c2 = __builtin_fmaxf(dq * load_uniform(ksc, u) * kLog2e, 1.17549435e-38f);
+      float c2 = __builtin_fmaxf(dq * load_uniform(ksc, u) * kLog2e, 1.17549435e-38f);
       const bool full = (k0 + kKBlock <= n) && (!CAUSAL || k0 + kKBlock - 1 <= wq_lo);
       if (!full) mask_scores<CAUSAL>(c.S, k0, n, qrow, gg);
-      softmax_phase<D, FP8>(c, c2);
+      float M = kMagicF;
+      if (SM) {
+        const int64_t row = hs * nqb + wqb;
+        const v2i fb = load_uniform2(a.qb_flags, row * (2 * nkb) + 2 * u);
+        if (fb.x | fb.y) {
+          // a half tile whose smoothing term did not fit the accumulator:
+          // every score of the tile becomes fp32 log2 units, s = (F - M)·c2
+          // (+ the fp32 term of a fallback half)
+          const float base = -(kMagicF * c2);
+          const float* fx = a.qb_fix + row * npad + k0;
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            const bool fall = s ? fb.y : fb.x;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 add = fall ? *reinterpret_cast<const float4*>(fx + 32 * s + 8 * q + 4 * gg)
+                                      : float4{0.f, 0.f, 0.f, 0.f};
+              const float av[4] = {add.x, add.y, add.z, add.w};
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int bits = c.S[s][4 * q + j];
+                c.S[s][4 * q + j] = __float_as_int(__builtin_fmaf(__int_as_float(bits), c2, av[j] + base));
+              }
+            }
+          }
+          c2 = 1.f;
+          M = 0.f;
+        }
+      }
+      softmax_phase<D, FP8, SM>(c, c2, M);
     }
   };
   // One workgroup barrier per tile.  Group A runs matrix(t) then softmax(t),
@@ -530,16 +620,19 @@ void attn_fwd_kernel(AttnArgs a) {
   // of tile t.
   for (int t = 0; t < ntiles; ++t) {
     if (lead && t + kAhead < ntiles)
-      issue_tile<D, FP8>(kbase, kbytes, vbase, vbytes, t + kAhead,
-                         smem + ((t + kAhead) % kRingStages) * G::STAGE, w, lane);
+      issue_tile<D, FP8, kThreads, SM>(kbase, kbytes, vbase, vbytes, t + kAhead,
+                                       smem + ((t + kAhead) % kRingStages) * G::STAGE, w, lane, ss);
     if (!lead && t > 0) softmax_step(t - 1);
     // One place for both MFMA parts keeps O and S in fixed registers.  At t = 0
     // the pending P is zero (O += 0·V of tile 0, which has landed); at t = nact
     // the QKᵀ result is not used.
     if (t <= nact && nact > 0)
-      matrix_both<D, FP8>(smem + (t % kRingStages) * G::STAGE,
-                          smem + ((t == 0 ? 0 : t - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, r32, gg, c.qf,
-                          c.S, c.pk16, c.pk8, c.O);
+      matrix_both<D, FP8, SM>(smem + (t % kRingStages) * G::STAGE,
+                              smem + ((t == 0 ? 0 : t - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, r32, gg,
+                              c.qf, c.S, c.pk16, c.pk8, c.O,
+                              reinterpret_cast<const v4i*>(smem + (t % kRingStages) * G::STAGE + G::KBYTES +
+                                                           G::VBYTES) +
+                                  32 * (wqb - q0 / kQBlock));
     if (lead) softmax_step(t);
     // tile t+1 landed before anyone's next matrix phase (later tiles may fly)
     if (lead) wait_tiles<L>(max(0, min(kAhead - 1, ntiles - 2 - t)));
@@ -622,7 +715,14 @@ __global__ __launch_bounds__(kThreads) void qk_tiles_kernel(const int8_t* __rest
 void launch_attn(const AttnArgs& a, bool causal, bool fp8, hipStream_t st) {
   const int64_t blocks = (int64_t)a.g.B * a.g.H * ceil_div(a.g.N, kAttnRows);
   const dim3 grid((unsigned)blocks), block(kAttnThreads);
-#define SAGE_ATTN(DD, F8, CS) hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS>), grid, block, 0, st, a)
+  const bool sm = a.qb_slots != nullptr;
+#define SAGE_ATTN(DD, F8, CS)                                                                  \
+  do {                                                                                         \
+    if (sm)                                                                                    \
+      hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS, true>), grid, block, 0, st, a);          \
+    else                                                                                       \
+      hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS, false>), grid, block, 0, st, a);         \
+  } while (0)
   if (a.g.d == 128) {
     if (!fp8) { if (causal) SAGE_ATTN(128, false, true); else SAGE_ATTN(128, false, false); }
     else { if (causal) SAGE_ATTN(128, true, true); else SAGE_ATTN(128, true, false); }

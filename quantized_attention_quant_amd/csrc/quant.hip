@@ -105,14 +105,22 @@ __device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
 
 // ---------------------------------------------------------------------------
 // Per-block INT8 of one block of ROWS tokens x D channels of fp32 values
-// x = fp16 input - shift; SMOOTH selects the K path (shift = token mean).
+// x = fp16 input - shift.  MODE selects the shift:
+//   kShiftNone  — Q without smoothing;
+//   kShiftKMean — K: the head-sequence's token mean (from the column sums),
+//                 written to mean[hs][D] by block 0;
+//   kShiftBlock — smoothed Q: the block's own token mean, written to
+//                 mean[hs][blk][D] (dtcms summary, section "SageAttention 2":
+//                 Q is smoothed as well).
 // Grid (ceil(Nmax/ROWS), H, B).
-template <int D, int ROWS, bool SMOOTH>
+enum { kShiftNone = 0, kShiftKMean = 1, kShiftBlock = 2 };
+
+template <int D, int ROWS, int MODE>
 __global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* __restrict__ x16, SeqGeom g,
                                                                const long long* __restrict__ colsum,
                                                                float out_scale_mul, int8_t* __restrict__ codes,
                                                                float* __restrict__ scales,
-                                                               float* __restrict__ kmean) {
+                                                               float* __restrict__ mean) {
   constexpr int CG = D / 8, RPP = kThreads / CG, PASSES = ROWS / RPP;
   static_assert(PASSES * RPP == ROWS, "block rows must be a multiple of rows per pass");
   const int b = blockIdx.z, h = blockIdx.y, blk = blockIdx.x;
@@ -133,17 +141,45 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* _
   float shift[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) shift[j] = 0.f;
-  if (SMOOTH) {
+  if (MODE == kShiftKMean) {
     // km = fp32(exact sum * 2^-24 / n): one fp64 divide per channel, one rounding
     __shared__ float km_s[D];
     if (threadIdx.x < D) {
       const float km = (float)((double)colsum[hs * D + threadIdx.x] * 0x1p-24 / (double)n);
       km_s[threadIdx.x] = km;
-      if (blk == 0) kmean[hs * D + threadIdx.x] = km;
+      if (blk == 0) mean[hs * D + threadIdx.x] = km;
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j) shift[j] = km_s[cg * 8 + j];
+  } else if (MODE == kShiftBlock) {
+    // the block's own mean, by the same exact rule: fp64 sums of fp16 values
+    // are exact (multiples of 2^-24 below 2^16, at most ROWS of them), one
+    // fp64 divide by the block's token count, one rounding to fp32
+    double acc[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = (uint32_t)raw[p][j];  // rows past n were loaded as zeros
+        acc[2 * j] += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+        acc[2 * j + 1] += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+      }
+    __shared__ double part[RPP][D];
+    __shared__ float qm_s[D];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[rr][cg * 8 + j] = acc[j];
+    __syncthreads();
+    if (threadIdx.x < D) {
+      double sum = 0.;  // exact in any order
+      for (int r = 0; r < RPP; ++r) sum += part[r][threadIdx.x];
+      const float qm = (float)(sum / (double)min(ROWS, n - t0));
+      qm_s[threadIdx.x] = qm;
+      mean[(hs * ceil_div(g.N, ROWS) + blk) * D + threadIdx.x] = qm;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) shift[j] = qm_s[cg * 8 + j];
   }
   // x = fp32(fp16) - shift; rows past n are zero (their codes are not stored)
   auto unpack = [&](int p, float (&x)[8]) {
@@ -358,26 +394,32 @@ void launch_zero(void* p, size_t bytes, hipStream_t st) {
 
 void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, float sm_scale,
                      int8_t* q_int8, int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean,
-                     long long* colsum, hipStream_t st) {
-  // gq: Q's geometry (H query heads); gk: K's (its own head count), same sequences
+                     float* q_mean, long long* colsum, hipStream_t st) {
+  // gq: Q's geometry (H query heads); gk: K's (its own head count), same
+  // sequences.  q_mean != nullptr selects Q smoothing.
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
   const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
   launch_zero(colsum, sizeof(long long) * (size_t)gk.B * gk.H * gk.d, st);
-  if (gq.d == 128) {
-    hipLaunchKernelGGL((k_colsum_kernel<128>), hs_grid(gk, kColsumChunk), dim3(kThreads), 0, st, k16, gk,
-                       reinterpret_cast<unsigned long long*>(colsum));
-    hipLaunchKernelGGL((quant_block_kernel<128, kQBlock, false>), hs_grid(gq, kQBlock), dim3(kThreads), 0, st,
-                       q16, gq, (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);
-    hipLaunchKernelGGL((quant_block_kernel<128, kKBlock, true>), hs_grid(gk, kKBlock), dim3(kThreads), 0, st,
-                       k16, gk, (const long long*)colsum, 1.0f, k_int8, k_scale, k_mean);
-  } else {
-    hipLaunchKernelGGL((k_colsum_kernel<64>), hs_grid(gk, kColsumChunk), dim3(kThreads), 0, st, k16, gk,
-                       reinterpret_cast<unsigned long long*>(colsum));
-    hipLaunchKernelGGL((quant_block_kernel<64, kQBlock, false>), hs_grid(gq, kQBlock), dim3(kThreads), 0, st,
-                       q16, gq, (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);
-    hipLaunchKernelGGL((quant_block_kernel<64, kKBlock, true>), hs_grid(gk, kKBlock), dim3(kThreads), 0, st,
-                       k16, gk, (const long long*)colsum, 1.0f, k_int8, k_scale, k_mean);
-  }
+  const dim3 gqb = hs_grid(gq, kQBlock), gkb = hs_grid(gk, kKBlock), blk(kThreads);
+  const long long* cs = colsum;
+#define SAGE_QUANT(DD)                                                                                          \
+  do {                                                                                                         \
+    hipLaunchKernelGGL((k_colsum_kernel<DD>), hs_grid(gk, kColsumChunk), blk, 0, st, k16, gk,                  \
+                       reinterpret_cast<unsigned long long*>(colsum));                                         \
+    if (q_mean)                                                                                                \
+      hipLaunchKernelGGL((quant_block_kernel<DD, kQBlock, kShiftBlock>), gqb, blk, 0, st, q16, gq,             \
+                         (const long long*)nullptr, sm_scale, q_int8, q_scale, q_mean);                        \
+    else                                                                                                       \
+      hipLaunchKernelGGL((quant_block_kernel<DD, kQBlock, kShiftNone>), gqb, blk, 0, st, q16, gq,              \
+                         (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);               \
+    hipLaunchKernelGGL((quant_block_kernel<DD, kKBlock, kShiftKMean>), gkb, blk, 0, st, k16, gk, cs, 1.0f,     \
+                       k_int8, k_scale, k_mean);                                                               \
+  } while (0)
+  if (gq.d == 128)
+    SAGE_QUANT(128);
+  else
+    SAGE_QUANT(64);
+#undef SAGE_QUANT
 }
 
 void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st) {

@@ -17,13 +17,35 @@ struct AttnArgs {
   float* lse;              // optional fp32 log-sum-exp per query row, or nullptr
   SeqGeom g;               // geometry of Q and O (H query heads)
   int kv_group;            // query heads per K/V head: K/V head of h is h / kv_group
+  // smoothed Q (all nullptr otherwise): per (Q block, key) accumulator initial
+  // values [B][H][nqb][npad], per (Q block, tile, half) fallback flags
+  // [B][H][nqb][2*nkb] and fp32 terms [B][H][nqb][npad] (npad = 64*nkb)
+  const int32_t* qb_slots = nullptr;
+  const float* qb_fix = nullptr;
+  const int32_t* qb_flags = nullptr;
+};
+
+// Inputs and outputs of the Q-smoothing term kernel (smooth_q.hip).
+struct QBiasArgs {
+  const uint16_t* k;       // fp16 K, Hkv heads
+  const float* k_mean;     // [B][Hkv][d]
+  const float* k_scale;    // [B][Hkv][nkb]
+  const float* q_mean;     // [B][H][nqb][d]
+  const float* q_scale;    // [B][H][nqb], softmax scale folded in
+  int32_t* slots;          // [B][H][nqb][npad]
+  float* fix;              // [B][H][nqb][npad]
+  int32_t* flags;          // [B][H][nqb][2*nkb]
+  SeqGeom g;               // geometry of Q (H query heads)
+  int kv_group;
+  float sm_log2e;          // softmax scale times log2(e)
+  int causal;              // skip (block, tile) pairs no query of the block sees
 };
 
 void launch_zero(void* p, size_t bytes, hipStream_t st);
 void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, float sm_scale,
-                     int8_t* q_int8,
-                     int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, long long* colsum,
-                     hipStream_t st);
+                     int8_t* q_int8, int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean,
+                     float* q_mean, long long* colsum, hipStream_t st);
+void launch_q_bias(const QBiasArgs& a, hipStream_t st);
 void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st);
 void launch_v_prepare(const SeqGeom& g, const void* v, const float* v_scale, bool fp8, bool rowmajor,
                       void* out, hipStream_t st);

@@ -56,9 +56,19 @@ def test_workspace_sizes():
     wv = sage.sage_attn_varlen_workspace_size(3, 200, 271, 2, 128, "fp16")
     assert wv >= 2 * 2 * 271 * 128
     offs = sage.sage_test_workspace_layout(False, 1, 2, 256, 0, 64, "fp8")
-    assert offs[7] == w8
+    assert offs[11] == w8
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs)
+    assert offs[7] == offs[8] == offs[9] == offs[10] == offs[11]   # no smoothed-Q regions
+    # a smoothed Q adds q_mean [B,H,nqb,d], initial values and fp32 terms
+    # [B,H,nqb,64·nkb] and flags [B,H,nqb,2·nkb]
+    ws = sage.sage_attn_workspace_size(1, 2, 256, 64, "fp8", smooth_q=True)
+    so = sage.sage_test_workspace_layout(False, 1, 2, 256, 0, 64, "fp8", smooth_q=True)
+    assert so[11] == ws > w8 and so[:7] == offs[:7]
+    assert so[8] - so[7] == 2 * 2 * 64 * 4
+    assert so[9] - so[8] == so[10] - so[9] == 2 * 2 * 256 * 4
+    assert so[11] - so[10] == 256 * ((2 * 2 * 8 * 4 + 255) // 256)
+    assert sage.sage_attn_varlen_workspace_size(3, 200, 271, 2, 128, "fp16", smooth_q=True) > wv
     # grouped K/V heads shrink every K/V region; invalid groupings give 0
     g = sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16", H_kv=1)
     assert 0 < g < sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16")
@@ -71,11 +81,11 @@ def test_workspace_sizes():
 
 def _fwd(**over):
     a = dict(q=ALIGNED, k=ALIGNED * 2, v=ALIGNED * 3, o=ALIGNED * 4, lse=None, B=1, H=2, Hkv=2, N=256, d=64,
-             layout=0, causal=0, pv=0, sm=0.0, ws=ALIGNED * 8, wsb=1 << 30, stream=None)
+             layout=0, causal=0, pv=0, smooth=0, sm=0.0, ws=ALIGNED * 8, wsb=1 << 30, stream=None)
     a.update(over)
     return sage.lib().sage_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
-                                    a["d"], a["layout"], a["causal"], a["pv"], a["sm"], a["ws"], a["wsb"],
-                                    a["stream"])
+                                    a["d"], a["layout"], a["causal"], a["pv"], a["smooth"], a["sm"], a["ws"],
+                                    a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("over,status", [
@@ -101,6 +111,8 @@ def _fwd(**over):
     (dict(Hkv=4), INVALID),                  # more K/V heads than query heads
     (dict(lse=ALIGNED * 4 + 2), INVALID),    # lse misaligned
     (dict(lse=ALIGNED * 4), INVALID),        # lse overlaps the output
+    (dict(smooth=1, d=96), INVALID),
+    (dict(smooth=1, wsb=sage.sage_attn_workspace_size(1, 2, 256, 64, "fp16")), WS_SMALL),  # needs more room
 ])
 def test_attn_fwd_rejects(over, status):
     assert _fwd(**over) == status
@@ -109,8 +121,8 @@ def test_attn_fwd_rejects(over, status):
 def test_varlen_rejects():
     L = sage.lib()
     f = L.sage_attn_varlen_fwd
-    args = [ALIGNED, ALIGNED * 2, ALIGNED * 3, ALIGNED * 4, None, ALIGNED * 5, 3, 128, 300, 2, 2, 64, 1, 0, 0.0,
-            ALIGNED * 8, 1 << 30, None]
+    args = [ALIGNED, ALIGNED * 2, ALIGNED * 3, ALIGNED * 4, None, ALIGNED * 5, 3, 128, 300, 2, 2, 64, 1, 0, 0,
+            0.0, ALIGNED * 8, 1 << 30, None]
     bad = list(args); bad[5] = None                 # cu_seqlens
     assert f(*bad) == INVALID
     bad = list(args); bad[6] = 0                    # nseq
@@ -121,25 +133,30 @@ def test_varlen_rejects():
     assert f(*bad) == INVALID
     bad = list(args); bad[10] = 3                   # H_kv does not divide H
     assert f(*bad) == INVALID
-    bad = list(args); bad[16] = 10
+    bad = list(args); bad[17] = 10
     assert f(*bad) == WS_SMALL
+    bad = list(args); bad[14] = 1; bad[17] = sage.sage_attn_varlen_workspace_size(3, 128, 300, 2, 64)
+    assert f(*bad) == WS_SMALL                      # smoothed Q needs a larger workspace
 
 
 def test_quant_rejects():
     L = sage.lib()
     st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, None, ALIGNED * 3, ALIGNED * 4,
-                         ALIGNED * 5, ALIGNED * 6, ALIGNED * 8, 1 << 20, None)
+                         ALIGNED * 5, ALIGNED * 6, None, ALIGNED * 8, 1 << 20, None)
     assert st == INVALID
     st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, ALIGNED * 9, ALIGNED * 3,
-                         ALIGNED * 4, ALIGNED * 5, ALIGNED * 6, ALIGNED * 8, 8, None)
+                         ALIGNED * 4, ALIGNED * 5, ALIGNED * 6, None, ALIGNED * 8, 8, None)
     assert st == WS_SMALL
+    st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, ALIGNED * 9, ALIGNED * 3,
+                         ALIGNED * 4, ALIGNED * 5, ALIGNED * 6, ALIGNED * 7 + 4, ALIGNED * 8, 1 << 20, None)
+    assert st == INVALID                            # q_mean misaligned
     st = L.sage_quant_v_fp8(ALIGNED, 1, 2, 256, 100, 0, None, 0, ALIGNED * 2, ALIGNED * 3, None)
     assert st == INVALID
     st = L.sage_test_qk_tiles(ALIGNED, ALIGNED * 2, 1, 1, 128, 64, ALIGNED * 3, 0, ALIGNED * 4, None)
     assert st == INVALID
-    arr = (ctypes.c_size_t * 8)()
-    assert L.sage_test_workspace_layout(0, 1, 1, 1, 128, 0, 80, 0, arr) == INVALID
-    assert L.sage_test_workspace_layout(0, 1, 4, 3, 128, 0, 64, 0, arr) == INVALID
+    arr = (ctypes.c_size_t * 12)()
+    assert L.sage_test_workspace_layout(0, 1, 1, 1, 128, 0, 80, 0, 0, arr) == INVALID
+    assert L.sage_test_workspace_layout(0, 1, 4, 3, 128, 0, 64, 0, 0, arr) == INVALID
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -598,3 +598,37 @@ def test_q_smooth_varlen_equals_per_sequence_dense():
         assert (quant["q_scale"][i, :, :nq] == dense["q_scale"][0]).all()
         assert (quant["q_mean"][i, :, :nq] == dense["q_mean"][0]).all()
         assert np.isnan(quant["q_mean"][i, :, nq:]).all()
+
+
+def test_fp8_code_envelope_covers_perturbed_scores():
+    """With score_eps, the fp8 output bound covers every output that scores
+    moved by at most ε per (Q block, key) can give (random trials, ε chosen
+    large enough to flip codes), is zero for ε = 0, and stays a small
+    fraction of the output."""
+    rng = np.random.default_rng(59)
+    n, d = 200, 16
+    q = (rng.standard_normal((n, d)) + 2 * rng.standard_normal(d)).astype(np.float16)
+    k = (rng.standard_normal((n, d)) * 2).astype(np.float16)
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    quant = O.quant_qk_dense(q[None, None], k[None, None], smooth_q=True)
+    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+    bias = O.q_smooth_bias(quant["q_mean"][0, 0], k, quant["k_mean"][0, 0], O.default_sm_scale(d))
+    vc, vs = O.quant_v_fp8(v)
+    rows = np.arange(n)
+    for causal in (False, True):
+        base, W = O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs, score_bias=bias,
+                                        score_eps=np.full_like(bias, 0.0))
+        assert (W == 0).all()
+        eps = np.full_like(bias, 2e-3)
+        base2, W = O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs, score_bias=bias, score_eps=eps)
+        assert (base2 == base).all()
+        assert W.max() > 0 and W.mean() < 2e-2
+        moved = 0
+        for trial in range(12):
+            pert = bias + rng.uniform(-1.0, 1.0, bias.shape) * eps
+            o = O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs, score_bias=pert)
+            diff = np.abs(o.astype(np.float64) - base.astype(np.float64))
+            slack = 2 ** -10 * np.abs(base.astype(np.float64)) + 1e-6   # fp16 output rounding
+            assert (diff <= W + slack).all(), (causal, trial, (diff - W - slack).max())
+            moved += int((diff > slack).sum())
+        assert moved > 0        # the trials do move codes: the envelope is exercised
