@@ -48,7 +48,9 @@ Readings where the pages are silent (each listed in the design notes):
   * Q smoothing (optional): the mean of each 128-token Q block (the K-mean
     rule applied to that block) is subtracted before the INT8 step, and the
     part of the score it carries, sm_scale * q̄ · (k - km) with the smoothed K
-    in fp32, is added back exactly (fp64) to every score of the block's rows.
+    in fp32, is added back exactly (fp64) to every score of the block's rows;
+  * per-token Q scales (optional, finer granularity): a Q "block" of one
+    token, the same quantiser on each row alone.
 """
 from __future__ import annotations
 
@@ -69,7 +71,7 @@ __all__ = [
     "quantize_int8_blocks", "quant_q", "quant_k", "quant_qk_dense", "quant_qk_varlen",
     "e4m3_decode", "e4m3_encode", "quant_v_fp8", "quant_v_fp8_dense", "quant_v_fp8_varlen",
     "qk_int", "sage_attention_rows", "sdpa_fp64_rows", "head_views_dense",
-    "head_views_varlen", "q_block_mean", "quant_q_smooth", "q_smooth_bias",
+    "head_views_varlen", "q_block_mean", "quant_q_smooth", "q_smooth_bias", "quant_q_per_token",
 ]
 
 
@@ -175,6 +177,15 @@ def q_block_mean(q: np.ndarray) -> np.ndarray:
     return np.stack([k_token_mean(q[..., b0:min(n, b0 + Q_BLOCK), :]) for b0 in range(0, n, Q_BLOCK)], axis=-2)
 
 
+def quant_q_per_token(q: np.ndarray, sm_scale: np.float32):
+    """Q with one scale per token ([DT] "SageAttention（v1）": per-block or
+    per-token quantisation of q and k; [DT] "SageAttention 2": finer, per
+    thread, granularity): the quantiser of ``quantize_int8_blocks`` with a
+    block of one row; sm_scale folded in.  Returns (codes, scale [..., n])."""
+    codes, scale = quantize_int8_blocks(q.astype(np.float32), 1)
+    return codes, (scale * np.float32(sm_scale)).astype(np.float32)
+
+
 def quant_q_smooth(q: np.ndarray, sm_scale: np.float32):
     """Q smoothed by its block mean, then per 128-token block INT8.
 
@@ -203,18 +214,23 @@ def q_smooth_bias(q_mean: np.ndarray, k: np.ndarray, k_mean: np.ndarray, sm_scal
 
 
 def quant_qk_dense(q: np.ndarray, k: np.ndarray, sm_scale: Optional[float] = None,
-                   smooth_q: bool = False) -> Dict[str, np.ndarray]:
+                   smooth_q: bool = False, q_per_token: bool = False) -> Dict[str, np.ndarray]:
     """Dense [B, H, N, d] fp16 inputs ([CS]: HND layout) -> INT8 tensors and scales.
 
-    Output shapes: q_int8, k_int8 [B,H,N,d]; q_scale [B,H,ceil(N/128)];
-    k_scale [B,H,ceil(N/64)]; k_mean [B,H,d]; with smooth_q also q_mean
-    [B,H,ceil(N/128),d].  K may have fewer heads than Q (its own shape).
+    Output shapes: q_int8, k_int8 [B,H,N,d]; q_scale [B,H,ceil(N/128)] (with
+    q_per_token [B,H,N]); k_scale [B,H,ceil(N/64)]; k_mean [B,H,d]; with
+    smooth_q also q_mean [B,H,ceil(N/128),d].  K may have fewer heads than Q
+    (its own shape).
     """
     d = q.shape[-1]
     sm = default_sm_scale(d) if not sm_scale or sm_scale <= 0 else np.float32(sm_scale)
     out = {}
+    if smooth_q and q_per_token:
+        raise ValueError("Q smoothing uses 128-token Q blocks")
     if smooth_q:
         qi, qs, out["q_mean"] = quant_q_smooth(q, sm)
+    elif q_per_token:
+        qi, qs = quant_q_per_token(q, sm)
     else:
         qi, qs = quant_q(q, sm)
     ki, ks, km = quant_k(k)
@@ -223,14 +239,16 @@ def quant_qk_dense(q: np.ndarray, k: np.ndarray, sm_scale: Optional[float] = Non
 
 
 def quant_qk_varlen(q: np.ndarray, k: np.ndarray, cu_seqlens: Sequence[int],
-                    sm_scale: Optional[float] = None, smooth_q: bool = False) -> Dict[str, np.ndarray]:
+                    sm_scale: Optional[float] = None, smooth_q: bool = False,
+                    q_per_token: bool = False) -> Dict[str, np.ndarray]:
     """Packed [H, T, d] inputs with sequence i on tokens [cu[i], cu[i+1]).
 
     Blocks and means never cross a sequence.  Scales and means are returned
     padded per sequence: q_scale [nseq,H,ceil(max/128)], k_scale
     [nseq,H,ceil(max/64)], k_mean [nseq,H,d], with smooth_q also q_mean
     [nseq,H,ceil(max/128),d]; padding entries are NaN (no value is defined
-    there).  K may have fewer heads than Q (its own shape).
+    there).  With q_per_token q_scale is per packed token, [H, T].  K may have
+    fewer heads than Q (its own shape).
     """
     H, T, d = q.shape
     Hk = k.shape[0]
@@ -241,7 +259,7 @@ def quant_qk_varlen(q: np.ndarray, k: np.ndarray, cu_seqlens: Sequence[int],
     sm = default_sm_scale(d) if not sm_scale or sm_scale <= 0 else np.float32(sm_scale)
     qi = np.zeros((H, T, d), np.int8)
     ki = np.zeros((Hk, T, d), np.int8)
-    qs = np.full((nseq, H, -(-mx // Q_BLOCK)), np.nan, np.float32)
+    qs = np.full((H, T) if q_per_token else (nseq, H, -(-mx // Q_BLOCK)), np.nan, np.float32)
     ks = np.full((nseq, Hk, -(-mx // K_BLOCK)), np.nan, np.float32)
     km = np.zeros((nseq, Hk, d), np.float32)
     qm = np.full((nseq, H, -(-mx // Q_BLOCK), d), np.nan, np.float32)
@@ -252,10 +270,15 @@ def quant_qk_varlen(q: np.ndarray, k: np.ndarray, cu_seqlens: Sequence[int],
         if smooth_q:
             c, s, m = quant_q_smooth(q[:, a:b], sm)
             qm[i, :, : m.shape[-2]] = m
+        elif q_per_token:
+            c, s = quant_q_per_token(q[:, a:b], sm)
         else:
             c, s = quant_q(q[:, a:b], sm)
         qi[:, a:b] = c
-        qs[i, :, : s.shape[-1]] = s
+        if q_per_token:
+            qs[:, a:b] = s
+        else:
+            qs[i, :, : s.shape[-1]] = s
         c, s, m = quant_k(k[:, a:b])
         ki[:, a:b] = c
         ks[i, :, : s.shape[-1]] = s
@@ -358,11 +381,11 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
                         k_scale: np.ndarray, v: np.ndarray, rows: Sequence[int], causal: bool,
                         pv_mode: str = "fp16", v_scale: Optional[np.ndarray] = None,
                         tile: int = KV_TILE, score_bias: Optional[np.ndarray] = None,
-                        score_eps: Optional[np.ndarray] = None):
+                        score_eps: Optional[np.ndarray] = None, q_block: int = Q_BLOCK):
     """Output rows of the quantised attention for one (sequence, head).
 
-    Inputs: q_int8/k_int8 [n, d] codes, q_scale [ceil(n/128)] (softmax scale
-    folded in), k_scale [ceil(n/64)]; v fp16 [n, d] (fp16 mode) or e4m3 codes
+    Inputs: q_int8/k_int8 [n, d] codes, q_scale [ceil(n/q_block)] (softmax
+    scale folded in; q_block = 1 for per-token Q scales), k_scale [ceil(n/64)]; v fp16 [n, d] (fp16 mode) or e4m3 codes
     [n, d] with v_scale [d] (fp8 mode).  ``rows``: query indices.
     ``score_bias``: with a smoothed Q, the [ceil(n/128), n] term of
     ``q_smooth_bias``, added to every score of a row of that Q block.
@@ -393,7 +416,7 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
     if pv_mode not in ("fp16", "fp8"):
         raise ValueError(pv_mode)
     qf = q_int8[rows].astype(np.float64)
-    dq = q_scale[rows // Q_BLOCK].astype(np.float64)
+    dq = q_scale[rows // q_block].astype(np.float64)
     if pv_mode == "fp8":
         if v_scale is None:
             raise ValueError("fp8 mode needs v_scale")
@@ -457,7 +480,8 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
 
 
 def score_lse_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndarray, k_scale: np.ndarray,
-                   rows: Sequence[int], causal: bool, score_bias: Optional[np.ndarray] = None) -> np.ndarray:
+                   rows: Sequence[int], causal: bool, score_bias: Optional[np.ndarray] = None,
+                   q_block: int = Q_BLOCK) -> np.ndarray:
     """Natural-log sum of exp of each row's dequantised scores over its visible
     keys, the quantity that merges partial softmax results over key ranges
     ([IP] §3.1 online softmax keeps it as (m, l): lse = m + log l):
@@ -471,7 +495,7 @@ def score_lse_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndarray, 
     n = k_int8.shape[0]
     keys = np.arange(n)
     acc = q_int8[rows].astype(np.float64) @ k_int8.astype(np.float64).T
-    s = acc * q_scale[rows // Q_BLOCK].astype(np.float64)[:, None] * k_scale[keys // K_BLOCK].astype(np.float64)[None, :]
+    s = acc * q_scale[rows // q_block].astype(np.float64)[:, None] * k_scale[keys // K_BLOCK].astype(np.float64)[None, :]
     if score_bias is not None:
         s = s + score_bias[rows // Q_BLOCK]
     if causal:
@@ -510,5 +534,6 @@ def head_views_dense(quant: Dict[str, np.ndarray], b: int, h: int):
 def head_views_varlen(quant: Dict[str, np.ndarray], cu_seqlens, i: int, h: int):
     a, b = int(cu_seqlens[i]), int(cu_seqlens[i + 1])
     n = b - a
-    return (quant["q_int8"][h, a:b], quant["q_scale"][i, h, : -(-n // Q_BLOCK)],
+    qs = quant["q_scale"]
+    return (quant["q_int8"][h, a:b], qs[h, a:b] if qs.ndim == 2 else qs[i, h, : -(-n // Q_BLOCK)],
             quant["k_int8"][h, a:b], quant["k_scale"][i, h, : -(-n // K_BLOCK)])

@@ -632,3 +632,87 @@ def test_fp8_code_envelope_covers_perturbed_scores():
             assert (diff <= W + slack).all(), (causal, trial, (diff - W - slack).max())
             moved += int((diff > slack).sum())
         assert moved > 0        # the trials do move codes: the envelope is exercised
+
+
+# --------------------------------------------------------------------------
+# Per-token Q scales
+# --------------------------------------------------------------------------
+def test_q_per_token_is_the_one_row_block_quantiser():
+    """Each row's codes and scale equal those of the row quantised alone (a
+    partial 128-token block of one row); the page's worked example as a row;
+    no row scale exceeds its 128-token block's."""
+    rng = np.random.default_rng(71)
+    q = (rng.standard_normal((300, 24)) * rng.choice([0.01, 1.0, 50.0], (300, 1))).astype(np.float16)
+    codes, scale = O.quant_q_per_token(q, np.float32(0.5))
+    assert scale.shape == (300,)
+    for i in range(0, 300, 13):
+        c1, s1 = O.quant_q(q[i:i + 1], np.float32(0.5))
+        assert (codes[i] == c1[0]).all() and scale[i] == s1[0]
+    ex = np.array([[0.1, 0.2, 0.15, 1000.0]], np.float16)
+    c, s = O.quant_q_per_token(ex, np.float32(1.0))
+    assert c.tolist() == [[0, 0, 0, 127]] and s[0] == np.float32(np.float32(1000.0) / np.float32(127))
+    _, sb = O.quant_q(q, np.float32(0.5))
+    assert (scale <= np.repeat(sb, 128)[:300]).all()
+
+
+def test_q_per_token_lossless_grid_matches_exact_attention():
+    """Rows on exact grids of their own step (each row attains 127) and a
+    zero-mean K on a per-block grid: per-token codes reproduce Q exactly, a
+    128-token block could not, and the method equals exact attention up to
+    fp16 P."""
+    rng = np.random.default_rng(72)
+    n, d = 192, 32
+    steps = 2.0 ** -rng.integers(2, 9, n)
+    qint = rng.integers(-126, 127, (n, d)).astype(np.float64)
+    qint[np.arange(n), rng.integers(0, d, n)] = 127
+    q = qint * steps[:, None]
+    half = rng.integers(-126, 127, (32, d)).astype(np.float64)
+    half[0, 0] = 127
+    k = np.concatenate([half, -half] * 3) * 2.0 ** -4
+    q16, k16 = q.astype(np.float16), k.astype(np.float16)
+    assert (q16.astype(np.float64) == q).all() and (k16.astype(np.float64) == k).all()
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    quant = O.quant_qk_dense(q16[None, None], k16[None, None], q_per_token=True)
+    qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+    sm = O.default_sm_scale(d)
+    assert (qi.astype(np.float64) * (qs / sm).astype(np.float64)[:, None] == q).all()
+    blk = O.quant_qk_dense(q16[None, None], k16[None, None])
+    bi, bs = blk["q_int8"][0, 0], blk["q_scale"][0, 0]
+    assert not (bi.astype(np.float64) * np.repeat(bs / sm, 128)[:n, None].astype(np.float64) == q).all()
+    for causal in (False, True):
+        ours = O.sage_attention_rows(qi, qs, ki, ks, v, np.arange(n), causal, q_block=1)
+        ref = O.sdpa_fp64_rows(q16, k16, v, np.arange(n), causal)
+        assert cos(ours, ref) >= 0.99999
+        assert np.abs(ours - ref).max() < 4e-3
+        lse = O.score_lse_rows(qi, qs, ki, ks, np.arange(n), causal, q_block=1)
+        s = (q @ k.T) * float(sm)
+        if causal:
+            s = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, s)
+        from scipy.special import logsumexp
+        assert np.abs(lse - logsumexp(s, axis=1)).max() < 1e-9
+
+
+def test_q_per_token_closer_to_exact_attention():
+    x = workloads.generate_custom(73, 1, 2, 600, 128, k_bias=3.0, q_bias=1.0)
+    for h in range(2):
+        q, k, v = x.q[0, h], x.k[0, h], x.v[0, h]
+        ref = O.sdpa_fp64_rows(q, k, v, np.arange(600), False)
+        blk = cos(_run(q, k, v, False), ref)
+        quant = O.quant_qk_dense(q[None, None], k[None, None], q_per_token=True)
+        qi, qs, ki, ks = O.head_views_dense(quant, 0, 0)
+        tok = cos(O.sage_attention_rows(qi, qs, ki, ks, v, np.arange(600), False, q_block=1), ref)
+        assert tok > blk >= 0.998
+
+
+def test_q_per_token_varlen_equals_per_sequence_dense():
+    x = workloads.generate_custom(74, 0, 2, 0, 64, lengths=[1, 130, 300])
+    cu = x.cu_seqlens
+    quant = O.quant_qk_varlen(x.q, x.k, cu, q_per_token=True)
+    assert quant["q_scale"].shape == (2, 431)
+    for i in range(3):
+        a, b = cu[i], cu[i + 1]
+        dense = O.quant_qk_dense(x.q[:, a:b][None], x.k[:, a:b][None], q_per_token=True)
+        assert (quant["q_int8"][:, a:b] == dense["q_int8"][0]).all()
+        assert (quant["q_scale"][:, a:b] == dense["q_scale"][0]).all()
+        qi, qs, _, _ = O.head_views_varlen(quant, cu, i, 1)
+        assert (qs == dense["q_scale"][0, 1]).all()
