@@ -213,6 +213,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--smooth-q", action="store_true",
                     help="time the forward with Q smoothing (the score term of Q's block mean added back)")
+    ap.add_argument("--q-per-token", action="store_true", help="time the forward with per-token Q scales")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates the HBM byte counters)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="DB",
@@ -250,8 +251,10 @@ def main():
         return
 
     w = workloads.get(args.workload)
-    sq = bool(args.smooth_q)
-    log(f"bench: workload {w.name}: {w.description}" + (" (Q smoothing)" if sq else ""))
+    sq, qt = bool(args.smooth_q), bool(args.q_per_token)
+    opts = dict(smooth_q=sq, q_per_token=qt)
+    log(f"bench: workload {w.name}: {w.description}" + (" (Q smoothing)" if sq else "") +
+        (" (per-token Q scales)" if qt else ""))
     x = workloads.generate(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -262,18 +265,18 @@ def main():
         cu = torch.from_numpy(x.cu_seqlens).to(dev)
         mx = int(x.lengths.max())
         ws = torch.empty(sage.sage_attn_varlen_workspace_size(w.B, mx, int(x.cu_seqlens[-1]), w.H, w.d, w.pv_mode,
-                                                              smooth_q=sq),
+                                                              **opts),
                          dtype=torch.uint8, device=dev)
 
         def step():
             sage.sage_attn_varlen_fwd(q, k, v, cu, mx, is_causal=w.causal, pv_mode=w.pv_mode, out=o, workspace=ws,
-                                      smooth_q=sq)
+                                      **opts)
     else:
-        ws = torch.empty(sage.sage_attn_workspace_size(w.B, w.H, w.N, w.d, w.pv_mode, smooth_q=sq),
+        ws = torch.empty(sage.sage_attn_workspace_size(w.B, w.H, w.N, w.d, w.pv_mode, **opts),
                          dtype=torch.uint8, device=dev)
 
         def step():
-            sage.sage_attn_fwd(q, k, v, is_causal=w.causal, pv_mode=w.pv_mode, out=o, workspace=ws, smooth_q=sq)
+            sage.sage_attn_fwd(q, k, v, is_causal=w.causal, pv_mode=w.pv_mode, out=o, workspace=ws, **opts)
 
     ops = attn_ops(w, x.lengths)
     for _ in range(args.warmup):
@@ -295,19 +298,19 @@ def main():
         # the fused attention kernel alone, re-run on the workspace the last step filled
         reps = max(args.steps, 5)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        sage.sage_test_attn_from_workspace(o, ws, is_causal=w.causal, pv_mode=w.pv_mode, smooth_q=sq)
+        sage.sage_test_attn_from_workspace(o, ws, is_causal=w.causal, pv_mode=w.pv_mode, **opts)
         e0.record(stream)
         for _ in range(reps):
-            sage.sage_test_attn_from_workspace(o, ws, is_causal=w.causal, pv_mode=w.pv_mode, smooth_q=sq)
+            sage.sage_test_attn_from_workspace(o, ws, is_causal=w.causal, pv_mode=w.pv_mode, **opts)
         e1.record(stream)
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / reps
         achieved = ops / (kern_ms * 1e-3) / 1e12
-        traffic = measured_traffic(w.name + ("+smooth_q" if sq else ""))
+        traffic = measured_traffic(w.name + ("+smooth_q" if sq else "") + ("+q_per_token" if qt else ""))
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
                     "kernel": f"attn_fwd_kernel<{w.d},{'fp8' if w.pv_mode == 'fp8' else 'fp16'}"
-                              f"{',smooth_q' if sq else ''}>",
+                              f"{',smooth_q' if sq else ''}{',q_per_token' if qt else ''}>",
                     "kernel_ms": round(kern_ms, 4),
                     "path_ceiling": round(path_ceiling(w.pv_mode), 1),
                     "frac_of_path_ceiling": round(achieved / path_ceiling(w.pv_mode), 4),
@@ -321,7 +324,7 @@ def main():
         cpu = cpu_baseline(w, x)
 
     config = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-              "pv_mode": w.pv_mode, "smooth_q": sq, "description": w.description}
+              "pv_mode": w.pv_mode, "smooth_q": sq, "q_per_token": qt, "description": w.description}
     if w.varlen:
         config["lengths"] = [int(n) for n in x.lengths]
     rec = {

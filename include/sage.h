@@ -67,6 +67,20 @@ typedef enum {
 } sage_status_t;
 
 typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1 } sage_pv_mode_t;
+
+/* Options, OR-ed into the `options` argument (0 = the default method).
+ *   SAGE_OPT_SMOOTH_Q: Q smoothing — each 128-token Q block's channel mean q̄
+ *     is subtracted before the INT8 step and the score term it carries,
+ *     sm_scale·q̄·(k − km), is added back to every score of the block's rows
+ *     (dtcms summary, section "SageAttention 2"; postsniper SageAttention2
+ *     bullets).
+ *   SAGE_OPT_Q_PER_TOKEN: one Q scale per token instead of per 128-token block
+ *     (dtcms summary: per-token q/k quantisation in "SageAttention（v1）", finer
+ *     granularity in "SageAttention 2"); q_scale is then indexed like the Q
+ *     rows: [B,H,N] dense, [H,T] varlen.
+ * The two are exclusive (SAGE_ERR_UNSUPPORTED): the smoothing term is carried
+ * in units of a per-block δQ.  Unknown bits -> SAGE_ERR_INVALID_ARGUMENT. */
+typedef enum { SAGE_OPT_SMOOTH_Q = 1, SAGE_OPT_Q_PER_TOKEN = 2 } sage_option_t;
 typedef enum { SAGE_LAYOUT_HND = 0 } sage_layout_t;
 
 /* A hipStream_t passed as an opaque pointer. */
@@ -95,9 +109,12 @@ const char* sage_status_string(sage_status_t s);
  *   * 2^-24 / n) per (sequence, head, channel); x = fp32(k) - km in fp32;
  *   scale = fp32(max|x| / 127) (IEEE division); code = clamp(rint(fp32(x /
  *   scale)), -127, 127); an all-zero block has scale 0 and codes 0.  Q the same
- *   without the mean, or — q_mean != NULL, Q smoothing — with the mean of each
- *   128-token block by the same exact rule over the block's own tokens,
- *   written to q_mean fp32 [B,H,ceil(N/128),d] (varlen: indexed by sequence).
+ *   without the mean, or — options SAGE_OPT_SMOOTH_Q, which requires q_mean !=
+ *   NULL (and NULL otherwise) — with the mean of each 128-token block by the
+ *   same exact rule over the block's own tokens, written to q_mean fp32
+ *   [B,H,ceil(N/128),d] (varlen: indexed by sequence); with
+ *   SAGE_OPT_Q_PER_TOKEN each Q row is its own block and q_scale is [B,H,N]
+ *   (varlen [H,T]).
  * workspace: device scratch of at least sage_quant_qk_workspace_size(B,H,d)
  *   bytes, 256-byte aligned; its contents on entry do not matter.
  */
@@ -105,8 +122,8 @@ size_t sage_quant_qk_workspace_size(int B, int H, int d);
 sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d,
                             sage_layout_t layout, const int32_t* cu_seqlens, int64_t total_tokens,
                             float sm_scale, int8_t* q_int8, int8_t* k_int8, float* q_scale,
-                            float* k_scale, float* k_mean, float* q_mean, void* workspace,
-                            size_t workspace_bytes, sage_stream_t stream);
+                            float* k_scale, float* k_mean, float* q_mean, int options,
+                            void* workspace, size_t workspace_bytes, sage_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * sage_quant_v_fp8 — per-channel e4m3 quantisation of V (the FP8-PV input).
@@ -132,10 +149,11 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
  *   (smoothed K: exact attention shifted by the row constant q·km·sm_scale),
  *   for merging partial results over key ranges; 4-byte aligned, no overlap.
  *   is_causal != 0 masks key j > query i (deepseek.csdn.net post: is_causal).
- *   pv_mode selects FP16 PV or FP8-e4m3 PV.  smooth_q != 0 selects Q
- *   smoothing: Q̂ and δQ come from Q minus its block mean and every score of a
- *   row of block b gets sm_scale·q̄_b·(k_j − km) added back (carried within
- *   one unit of δQ·δK); the workspace is then larger.  sm_scale <= 0 ->
+ *   pv_mode selects FP16 PV or FP8-e4m3 PV.  options (sage_option_t bits):
+ *   SAGE_OPT_SMOOTH_Q — Q̂ and δQ come from Q minus its block mean and every
+ *   score of a row of block b gets sm_scale·q̄_b·(k_j − km) added back
+ *   (carried within one unit of δQ·δK; the workspace is then larger);
+ *   SAGE_OPT_Q_PER_TOKEN — one Q scale per query row.  sm_scale <= 0 ->
  *   1/sqrt(d).
  *   The pre-pass (smoothing, quantisation, V packing) writes into the
  *   caller's workspace of at least sage_attn_workspace_size(...) bytes; its
@@ -147,10 +165,10 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
  *   Nothing is launched on error.  Asynchronous on `stream`.
  */
 size_t sage_attn_workspace_size(int B, int H, int H_kv, int N, int d, sage_pv_mode_t pv_mode,
-                                int smooth_q);
+                                int options);
 sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                             int B, int H, int H_kv, int N, int d, sage_layout_t layout,
-                            int is_causal, sage_pv_mode_t pv_mode, int smooth_q, float sm_scale,
+                            int is_causal, sage_pv_mode_t pv_mode, int options, float sm_scale,
                             void* workspace, size_t workspace_bytes, sage_stream_t stream);
 
 /* ------------------------------------------------------------------------
@@ -163,11 +181,11 @@ sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o
  *   and the causal mask are per sequence.  Empty sequences are allowed.
  */
 size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H,
-                                       int H_kv, int d, sage_pv_mode_t pv_mode, int smooth_q);
+                                       int H_kv, int d, sage_pv_mode_t pv_mode, int options);
 sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o,
                                    float* lse, const int32_t* cu_seqlens, int nseq,
                                    int max_seqlen, int64_t total_tokens, int H, int H_kv, int d,
-                                   int is_causal, sage_pv_mode_t pv_mode, int smooth_q,
+                                   int is_causal, sage_pv_mode_t pv_mode, int options,
                                    float sm_scale, void* workspace, size_t workspace_bytes,
                                    sage_stream_t stream);
 
@@ -178,7 +196,7 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  *   (varlen == 0) or sage_attn_varlen_fwd (varlen != 0) workspace, of
  *   [0] q_int8, [1] k_int8, [2] q_scale, [3] k_scale, [4] k_mean,
  *   [5] packed V, [6] v_scale (fp8 mode; an empty region in fp16 mode),
- *   and, with smooth_q (empty regions otherwise), [7] q_mean fp32
+ *   and, with SAGE_OPT_SMOOTH_Q (empty regions otherwise), [7] q_mean fp32
  *   [B,H,nqb,d], [8] accumulator initial values int32 [B,H,nqb,npad],
  *   [9] fp32 fallback terms [B,H,nqb,npad], [10] fallback flags int32
  *   [B,H,nqb,2·nkb] (nqb = ceil(N/128), nkb = ceil(N/64), npad = 64·nkb;
@@ -200,17 +218,17 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
 /*
  * sage_test_attn_from_workspace: launch only the fused attention kernel on a
  *   workspace that a preceding sage_attn_fwd call with the same B,H,H_kv,N,d,
- *   is_causal, pv_mode and smooth_q has filled (its pre-pass results are reused as they
+ *   is_causal, pv_mode and options has filled (its pre-pass results are reused as they
  *   are); writes o fp16 [B,H,N,d] (no LSE).  Used to time the attention
  *   kernel alone.  Same validation as sage_attn_fwd.
  */
 sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int N, int d,
-                                            int is_causal, sage_pv_mode_t pv_mode, int smooth_q,
+                                            int is_causal, sage_pv_mode_t pv_mode, int options,
                                             const void* workspace, size_t workspace_bytes,
                                             sage_stream_t stream);
 sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int N,
                                          int64_t total_tokens, int d, sage_pv_mode_t pv_mode,
-                                         int smooth_q, size_t offsets_out[12]);
+                                         int options, size_t offsets_out[12]);
 sage_status_t sage_test_qk_tiles(const int8_t* q_int8, const int8_t* k_int8, int B, int H, int N,
                                  int d, const int32_t* tile_list, int n_tiles, int32_t* out,
                                  sage_stream_t stream);

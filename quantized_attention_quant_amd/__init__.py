@@ -28,6 +28,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsage.so")
 PV_MODES = {"fp16": 0, "fp8": 1}
 LAYOUT_HND = 0
+OPT_SMOOTH_Q = 1        # sage_option_t bits
+OPT_Q_PER_TOKEN = 2
+
+
+def _options(smooth_q: bool, q_per_token: bool) -> int:
+    return (OPT_SMOOTH_Q if smooth_q else 0) | (OPT_Q_PER_TOKEN if q_per_token else 0)
 
 # exported symbol -> (restype, argtypes)
 _c = ctypes
@@ -36,7 +42,7 @@ SIGNATURES = {
     "sage_status_string": (_c.c_char_p, [_c.c_int]),
     "sage_quant_qk_workspace_size": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int]),
     "sage_quant_qk": (_c.c_int, [_P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P, _c.c_int64,
-                                 _c.c_float, _P, _P, _P, _P, _P, _P, _P, _c.c_size_t, _P]),
+                                 _c.c_float, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t, _P]),
     "sage_quant_v_fp8": (_c.c_int, [_P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P, _c.c_int64,
                                     _P, _P, _P]),
     "sage_attn_workspace_size": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
@@ -135,12 +141,12 @@ def sage_quant_qk_workspace_size(B: int, H: int, d: int) -> int:
 def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
                   max_seqlen: Optional[int] = None, sm_scale: float = 0.0,
                   workspace: Optional[torch.Tensor] = None, stream=None,
-                  smooth_q: bool = False) -> Dict[str, torch.Tensor]:
+                  smooth_q: bool = False, q_per_token: bool = False) -> Dict[str, torch.Tensor]:
     """Dense q,k [B,H,N,d] or varlen packed [H,T,d] (+cu_seqlens, max_seqlen).
 
     Returns dict(q_int8, k_int8, q_scale, k_scale, k_mean[, q_mean with
     smooth_q]) as device tensors in the layouts documented for the C entry
-    point."""
+    point (q_scale per token with q_per_token)."""
     L = lib()
     if cu_seqlens is None:
         _need(q, "q", torch.float16, 4)
@@ -157,7 +163,8 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, cu_seqlens: Optional[torch.T
     out = dict(
         q_int8=torch.empty(q.shape, dtype=torch.int8, device=dev),
         k_int8=torch.empty(q.shape, dtype=torch.int8, device=dev),
-        q_scale=torch.empty((B, H, -(-N // 128)), dtype=torch.float32, device=dev),
+        q_scale=torch.empty(tuple(q.shape[:-1]) if q_per_token else (B, H, -(-N // 128)), dtype=torch.float32,
+                            device=dev),
         k_scale=torch.empty((B, H, -(-N // 64)), dtype=torch.float32, device=dev),
         k_mean=torch.empty((B, H, d), dtype=torch.float32, device=dev),
     )
@@ -167,7 +174,8 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, cu_seqlens: Optional[torch.T
     st = L.sage_quant_qk(q.data_ptr(), k.data_ptr(), B, H, N, d, LAYOUT_HND, _ptr(cu_seqlens), T, float(sm_scale),
                          out["q_int8"].data_ptr(), out["k_int8"].data_ptr(), out["q_scale"].data_ptr(),
                          out["k_scale"].data_ptr(), out["k_mean"].data_ptr(), _ptr(out.get("q_mean")),
-                         ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+                         _options(smooth_q, q_per_token), ws.data_ptr(), ws.numel() * ws.element_size(),
+                         _stream(stream))
     _check(st, "sage_quant_qk")
     return out
 
@@ -192,9 +200,9 @@ def sage_quant_v_fp8(v: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
 
 
 def sage_attn_workspace_size(B: int, H: int, N: int, d: int, pv_mode: str = "fp16",
-                             H_kv: Optional[int] = None, smooth_q: bool = False) -> int:
+                             H_kv: Optional[int] = None, smooth_q: bool = False, q_per_token: bool = False) -> int:
     return int(lib().sage_attn_workspace_size(B, H, H if H_kv is None else H_kv, N, d, PV_MODES[pv_mode],
-                                              int(bool(smooth_q))))
+                                              _options(smooth_q, q_per_token)))
 
 
 def _lse_out(return_lse: bool, lse: Optional[torch.Tensor], shape, device) -> Optional[torch.Tensor]:
@@ -209,10 +217,10 @@ def _lse_out(return_lse: bool, lse: Optional[torch.Tensor], shape, device) -> Op
 def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
                   pv_mode: str = "fp16", sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None, stream=None, return_lse: bool = False,
-                  lse: Optional[torch.Tensor] = None, smooth_q: bool = False):
+                  lse: Optional[torch.Tensor] = None, smooth_q: bool = False, q_per_token: bool = False):
     """Dense forward: q fp16 [B,H,N,d], k and v fp16 [B,H_kv,N,d] (H_kv divides H).
-    smooth_q selects Q smoothing.  Returns o fp16 [B,H,N,d], or (o, lse fp32
-    [B,H,N]) when return_lse or lse is given."""
+    smooth_q selects Q smoothing, q_per_token per-token Q scales.  Returns o
+    fp16 [B,H,N,d], or (o, lse fp32 [B,H,N]) when return_lse or lse is given."""
     L = lib()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need(t, name, torch.float16, 4)
@@ -225,9 +233,10 @@ def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: 
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.float16, 4)
     lse_t = _lse_out(return_lse, lse, (B, H, N), q.device)
-    ws = _alloc_ws(sage_attn_workspace_size(B, H, N, d, pv_mode, H_kv, smooth_q), q.device, workspace)
+    opts = _options(smooth_q, q_per_token)
+    ws = _alloc_ws(sage_attn_workspace_size(B, H, N, d, pv_mode, H_kv, smooth_q, q_per_token), q.device, workspace)
     st = L.sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse_t), B, H, H_kv, N, d,
-                         LAYOUT_HND, int(bool(is_causal)), PV_MODES[pv_mode], int(bool(smooth_q)), float(sm_scale),
+                         LAYOUT_HND, int(bool(is_causal)), PV_MODES[pv_mode], opts, float(sm_scale),
                          ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sage_attn_fwd")
     return o if lse_t is None else (o, lse_t)
@@ -235,16 +244,16 @@ def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: 
 
 def sage_attn_varlen_workspace_size(nseq: int, max_seqlen: int, total_tokens: int, H: int, d: int,
                                     pv_mode: str = "fp16", H_kv: Optional[int] = None,
-                                    smooth_q: bool = False) -> int:
+                                    smooth_q: bool = False, q_per_token: bool = False) -> int:
     return int(lib().sage_attn_varlen_workspace_size(nseq, max_seqlen, total_tokens, H, H if H_kv is None else H_kv,
-                                                     d, PV_MODES[pv_mode], int(bool(smooth_q))))
+                                                     d, PV_MODES[pv_mode], _options(smooth_q, q_per_token)))
 
 
 def sage_attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens: torch.Tensor,
                          max_seqlen: int, is_causal: bool = False, pv_mode: str = "fp16", sm_scale: float = 0.0,
                          out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                          stream=None, return_lse: bool = False, lse: Optional[torch.Tensor] = None,
-                         smooth_q: bool = False):
+                         smooth_q: bool = False, q_per_token: bool = False):
     """Packed forward: q fp16 [H,T,d], k and v fp16 [H_kv,T,d], int32 cu_seqlens [nseq+1]
     (device).  Returns o fp16 [H,T,d], or (o, lse fp32 [H,T])."""
     L = lib()
@@ -257,10 +266,11 @@ def sage_attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_s
     o = torch.empty_like(q) if out is None else out
     _need(o, "out", torch.float16, 3)
     lse_t = _lse_out(return_lse, lse, (H, T), q.device)
-    ws = _alloc_ws(sage_attn_varlen_workspace_size(nseq, N, T, H, d, pv_mode, H_kv, smooth_q), q.device, workspace)
+    ws = _alloc_ws(sage_attn_varlen_workspace_size(nseq, N, T, H, d, pv_mode, H_kv, smooth_q, q_per_token), q.device,
+                   workspace)
     st = L.sage_attn_varlen_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse_t),
                                 cu_seqlens.data_ptr(), nseq, N, T, H, H_kv, d, int(bool(is_causal)),
-                                PV_MODES[pv_mode], int(bool(smooth_q)), float(sm_scale), ws.data_ptr(),
+                                PV_MODES[pv_mode], _options(smooth_q, q_per_token), float(sm_scale), ws.data_ptr(),
                                 ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sage_attn_varlen_fwd")
     return o if lse_t is None else (o, lse_t)
@@ -268,11 +278,11 @@ def sage_attn_varlen_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_s
 
 def sage_test_workspace_layout(varlen: bool, B: int, H: int, N: int, total_tokens: int, d: int,
                                pv_mode: str = "fp16", H_kv: Optional[int] = None,
-                               smooth_q: bool = False) -> Sequence[int]:
+                               smooth_q: bool = False, q_per_token: bool = False) -> Sequence[int]:
     """Byte offsets [0..10] of the workspace regions and [11] its total size."""
     arr = (ctypes.c_size_t * 12)()
     st = lib().sage_test_workspace_layout(int(bool(varlen)), B, H, H if H_kv is None else H_kv, N, total_tokens, d,
-                                          PV_MODES[pv_mode], int(bool(smooth_q)), arr)
+                                          PV_MODES[pv_mode], _options(smooth_q, q_per_token), arr)
     _check(st, "sage_test_workspace_layout")
     return list(arr)
 
@@ -294,13 +304,13 @@ def sage_test_qk_tiles(q_int8: torch.Tensor, k_int8: torch.Tensor, tile_list: to
 
 def sage_test_attn_from_workspace(out: torch.Tensor, workspace: torch.Tensor, is_causal: bool = False,
                                   pv_mode: str = "fp16", stream=None, H_kv: Optional[int] = None,
-                                  smooth_q: bool = False) -> torch.Tensor:
+                                  smooth_q: bool = False, q_per_token: bool = False) -> torch.Tensor:
     """Run only the fused attention kernel on a workspace filled by sage_attn_fwd
     (same shapes and options); out fp16 [B,H,N,d] is written and returned."""
     _need(out, "out", torch.float16, 4)
     B, H, N, d = out.shape
     st = lib().sage_test_attn_from_workspace(out.data_ptr(), B, H, H if H_kv is None else H_kv, N, d,
-                                             int(bool(is_causal)), PV_MODES[pv_mode], int(bool(smooth_q)),
+                                             int(bool(is_causal)), PV_MODES[pv_mode], _options(smooth_q, q_per_token),
                                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                              _stream(stream))
     _check(st, "sage_test_attn_from_workspace")

@@ -38,7 +38,9 @@ struct WsLayout {
   size_t total;
 };
 
-WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d, bool fp8, bool smooth_q) {
+WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d, bool fp8, int options) {
+  const bool smooth_q = (options & SAGE_OPT_SMOOTH_Q) != 0;
+  const bool q_per_token = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
   const int64_t tokens = varlen ? (int64_t)H * T : (int64_t)B * H * N;
   const int64_t ktokens = varlen ? (int64_t)Hkv * T : (int64_t)B * Hkv * N;
   const int64_t nqb = ceil_div64(N, sage::kQBlock), nkb = ceil_div64(N, sage::kKBlock);
@@ -48,7 +50,7 @@ WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d
   const size_t sizes[kWsRegions] = {
       (size_t)(tokens * d),
       (size_t)(ktokens * d),
-      sizeof(float) * (size_t)B * H * nqb,
+      sizeof(float) * (q_per_token ? (size_t)tokens : (size_t)B * H * nqb),
       sizeof(float) * (size_t)B * Hkv * nkb,
       sizeof(float) * (size_t)B * Hkv * d,
       (size_t)vtiles * sage::kKBlock * d * (fp8 ? 1 : 2),
@@ -71,6 +73,11 @@ WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d
 
 // K/V heads: 1 <= Hkv <= H and Hkv divides H (grouped-query / multi-query).
 inline bool kv_heads_ok(int H, int Hkv) { return Hkv >= 1 && Hkv <= H && H % Hkv == 0; }
+
+constexpr int kKnownOptions = SAGE_OPT_SMOOTH_Q | SAGE_OPT_Q_PER_TOKEN;
+inline bool options_known(int o) { return (o & ~kKnownOptions) == 0; }
+// Q smoothing carries its term in units of a per-block δQ: not with per-token scales.
+inline bool options_supported(int o) { return (o & kKnownOptions) != kKnownOptions; }
 
 sage_status_t check_dims(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARGUMENT;
@@ -107,7 +114,7 @@ sage_status_t finish(hipStream_t st) {
 // Shared body of the dense and varlen forward.  g: geometry of Q and O; K and V
 // have Hkv heads over the same sequences.
 sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o, float* lse, const SeqGeom& g,
-                           int Hkv, bool varlen, int is_causal, sage_pv_mode_t pv_mode, int smooth_q,
+                           int Hkv, bool varlen, int is_causal, sage_pv_mode_t pv_mode, int options,
                            float sm_scale, void* workspace, size_t workspace_bytes, sage_stream_t stream) noexcept {
   if (!q || !k || !v || !o || !workspace) return SAGE_ERR_INVALID_ARGUMENT;
   if (!kv_heads_ok(g.H, Hkv)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -115,11 +122,14 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return SAGE_ERR_INVALID_ARGUMENT;
   if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!options_supported(options)) return SAGE_ERR_UNSUPPORTED;
   float sm;
   if (!resolve_sm_scale(sm_scale, g.d, &sm)) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
-  const bool sq = smooth_q != 0;
-  const WsLayout L = make_layout(varlen, g.B, g.H, Hkv, g.N, g.T, g.d, fp8, sq);
+  const bool sq = (options & SAGE_OPT_SMOOTH_Q) != 0;
+  const bool qtok = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
+  const WsLayout L = make_layout(varlen, g.B, g.H, Hkv, g.N, g.T, g.d, fp8, options);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const int64_t rows = varlen ? (int64_t)g.H * g.T : (int64_t)g.B * g.H * g.N;
   const size_t tensor_bytes = (size_t)rows * g.d * 2;
@@ -151,7 +161,7 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
 
   SeqGeom gk = g;
   gk.H = Hkv;
-  sage::launch_quant_qk(g, gk, q, k, sm, q8, k8, qs, ks, km, qm, colsum, st);
+  sage::launch_quant_qk(g, gk, q, k, sm, q8, k8, qs, ks, km, qm, qtok, colsum, st);
   if (sq) {
     const sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, ks, qm, qs, slots, fix, flags, g, g.H / Hkv,
                              (float)((double)sm * 1.4426950408889634), is_causal != 0};
@@ -160,6 +170,7 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   if (fp8) sage::launch_v_scale(gk, v, vs, st);
   sage::launch_v_prepare(gk, v, vs, fp8, /*rowmajor=*/false, vp, st);
   sage::AttnArgs a{q8, k8, qs, ks, vp, vs, static_cast<uint16_t*>(o), lse, g, g.H / Hkv};
+  a.q_per_token = qtok;
   if (sq) {
     a.qb_slots = slots;
     a.qb_fix = fix;
@@ -204,7 +215,7 @@ size_t sage_quant_qk_workspace_size(int B, int H, int d) {
 sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, int d, sage_layout_t layout,
                             const int32_t* cu_seqlens, int64_t total_tokens, float sm_scale, int8_t* q_int8,
                             int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean, float* q_mean,
-                            void* workspace, size_t workspace_bytes, sage_stream_t stream) {
+                            int options, void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
   SeqGeom g;
   if (cu_seqlens) {
@@ -217,6 +228,9 @@ sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, i
   }
   if (!q || !k || !q_int8 || !k_int8 || !q_scale || !k_scale || !k_mean || !workspace)
     return SAGE_ERR_INVALID_ARGUMENT;
+  if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!options_supported(options)) return SAGE_ERR_UNSUPPORTED;
+  if (((options & SAGE_OPT_SMOOTH_Q) != 0) != (q_mean != nullptr)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(k) || !aligned16(q_int8) || !aligned16(k_int8) || !aligned16(q_scale) ||
       !aligned16(k_scale) || !aligned16(k_mean) || !aligned16(q_mean) ||
       (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
@@ -227,7 +241,7 @@ sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, i
   if (cu_seqlens && total_tokens == 0) return SAGE_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   sage::launch_quant_qk(g, g, q, k, sm, q_int8, k_int8, q_scale, k_scale, k_mean, q_mean,
-                        static_cast<long long*>(workspace), st);
+                        (options & SAGE_OPT_Q_PER_TOKEN) != 0, static_cast<long long*>(workspace), st);
   return finish(st);
 }
 
@@ -253,52 +267,54 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
   return finish(st);
 }
 
-size_t sage_attn_workspace_size(int B, int H, int H_kv, int N, int d, sage_pv_mode_t pv_mode, int smooth_q) {
+size_t sage_attn_workspace_size(int B, int H, int H_kv, int N, int d, sage_pv_mode_t pv_mode, int options) {
   if (check_dims(B, H, N, d) != SAGE_OK || !kv_heads_ok(H, H_kv)) return 0;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
-  return make_layout(false, B, H, H_kv, N, 0, d, pv_mode == SAGE_PV_FP8_E4M3, smooth_q != 0).total;
+  if (!options_known(options) || !options_supported(options)) return 0;
+  return make_layout(false, B, H, H_kv, N, 0, d, pv_mode == SAGE_PV_FP8_E4M3, options).total;
 }
 
 sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                             int H_kv, int N, int d, sage_layout_t layout, int is_causal, sage_pv_mode_t pv_mode,
-                            int smooth_q, float sm_scale, void* workspace, size_t workspace_bytes,
+                            int options, float sm_scale, void* workspace, size_t workspace_bytes,
                             sage_stream_t stream) {
   if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
   const sage_status_t s = check_dims(B, H, N, d);
   if (s != SAGE_OK) return s;
   const SeqGeom g{nullptr, B, H, N, d, 0};
-  return attn_forward(q, k, v, o, lse, g, H_kv, false, is_causal, pv_mode, smooth_q, sm_scale, workspace,
+  return attn_forward(q, k, v, o, lse, g, H_kv, false, is_causal, pv_mode, options, sm_scale, workspace,
                       workspace_bytes, stream);
 }
 
 size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H, int H_kv, int d,
-                                       sage_pv_mode_t pv_mode, int smooth_q) {
+                                       sage_pv_mode_t pv_mode, int options) {
   if (nseq < 1 || total_tokens < 0 || check_dims(nseq, H, max_seqlen, d) != SAGE_OK || !kv_heads_ok(H, H_kv))
     return 0;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
-  return make_layout(true, nseq, H, H_kv, max_seqlen, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3, smooth_q != 0)
-      .total;
+  if (!options_known(options) || !options_supported(options)) return 0;
+  return make_layout(true, nseq, H, H_kv, max_seqlen, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3, options).total;
 }
 
 sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                    const int32_t* cu_seqlens, int nseq, int max_seqlen, int64_t total_tokens, int H,
-                                   int H_kv, int d, int is_causal, sage_pv_mode_t pv_mode, int smooth_q,
+                                   int H_kv, int d, int is_causal, sage_pv_mode_t pv_mode, int options,
                                    float sm_scale, void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   SeqGeom g;
   const sage_status_t s = varlen_geom(cu_seqlens, nseq, max_seqlen, total_tokens, H, d, &g);
   if (s != SAGE_OK) return s;
-  return attn_forward(q, k, v, o, lse, g, H_kv, true, is_causal, pv_mode, smooth_q, sm_scale, workspace,
+  return attn_forward(q, k, v, o, lse, g, H_kv, true, is_causal, pv_mode, options, sm_scale, workspace,
                       workspace_bytes, stream);
 }
 
 sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int N, int64_t total_tokens, int d,
-                                         sage_pv_mode_t pv_mode, int smooth_q, size_t offsets_out[12]) {
+                                         sage_pv_mode_t pv_mode, int options, size_t offsets_out[12]) {
   if (!offsets_out) return SAGE_ERR_INVALID_ARGUMENT;
   if (check_dims(B, H, N, d) != SAGE_OK || !kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
   if (varlen && total_tokens < 0) return SAGE_ERR_INVALID_ARGUMENT;
-  const WsLayout L =
-      make_layout(varlen != 0, B, H, H_kv, N, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3, smooth_q != 0);
+  if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!options_supported(options)) return SAGE_ERR_UNSUPPORTED;
+  const WsLayout L = make_layout(varlen != 0, B, H, H_kv, N, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3, options);
   for (int i = 0; i < 7; ++i) offsets_out[i] = L.off[i];
   for (int i = 8; i < kWsRegions; ++i) offsets_out[i - 1] = L.off[i];
   offsets_out[11] = L.total;
@@ -306,7 +322,7 @@ sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int
 }
 
 sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int N, int d, int is_causal,
-                                            sage_pv_mode_t pv_mode, int smooth_q, const void* workspace,
+                                            sage_pv_mode_t pv_mode, int options, const void* workspace,
                                             size_t workspace_bytes, sage_stream_t stream) {
   const sage_status_t s = check_dims(B, H, N, d);
   if (s != SAGE_OK) return s;
@@ -314,8 +330,10 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
   if (!o || !workspace || !aligned16(o) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
     return SAGE_ERR_INVALID_ARGUMENT;
   if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!options_supported(options)) return SAGE_ERR_UNSUPPORTED;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
-  const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, fp8, smooth_q != 0);
+  const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, fp8, options);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const size_t tensor_bytes = (size_t)B * H * N * d * 2;
   if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
@@ -325,7 +343,8 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
                    reinterpret_cast<const float*>(ws + L.off[2]), reinterpret_cast<const float*>(ws + L.off[3]),
                    reinterpret_cast<const uint8_t*>(ws + L.off[5]), reinterpret_cast<const float*>(ws + L.off[6]),
                    static_cast<uint16_t*>(o), nullptr, g, H / H_kv};
-  if (smooth_q) {
+  a.q_per_token = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
+  if (options & SAGE_OPT_SMOOTH_Q) {
     a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[9]);
     a.qb_fix = reinterpret_cast<const float*>(ws + L.off[10]);
     a.qb_flags = reinterpret_cast<const int32_t*>(ws + L.off[11]);

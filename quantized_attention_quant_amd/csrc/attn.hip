@@ -489,14 +489,21 @@ __device__ __forceinline__ void wait_tiles(int pending) {
 
 // d=64 fits 128 VGPRs, so two workgroups share a CU (four waves per SIMD) and
 // their independent phases fill each other's stalls; d=128 needs ~180, and so
-// does d=64 with a smoothed Q (its accumulator initial values would spill).
-template <int D, bool SM>
-constexpr int kAttnWavesPerSimd = (D == 64 && !SM) ? 4 : 2;
+// does d=64 with a smoothed Q (its accumulator initial values would spill) or
+// with per-token Q scales and FP8 PV (one or two spilled registers).
+template <int D, bool LOW_OCCUPANCY>
+constexpr int kAttnWavesPerSimd = (D == 64 && !LOW_OCCUPANCY) ? 4 : 2;
 
-template <int D, bool FP8, bool CAUSAL, bool SM>
+// How Q is scaled: per 128-token block, per block with the smoothing term, or
+// per token (one scale per query row, so the per-tile factor is per lane).
+enum { kQmBlock = 0, kQmSmooth = 1, kQmToken = 2 };
+
+template <int D, bool FP8, bool CAUSAL, int QM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads),
-                          amdgpu_waves_per_eu(kAttnWavesPerSimd<D, SM>, kAttnWavesPerSimd<D, SM>)))
+                          amdgpu_waves_per_eu(kAttnWavesPerSimd<D, QM == kQmSmooth || (QM == kQmToken && FP8)>,
+                                              kAttnWavesPerSimd<D, QM == kQmSmooth || (QM == kQmToken && FP8)>)))
 void attn_fwd_kernel(AttnArgs a) {
+  constexpr bool SM = QM == kQmSmooth;
   constexpr int DT = D / 32;  // 32-wide d tiles of the output
   using G = TileGeom<D, FP8, kThreads, SM>;  // tiles are streamed by the 4 waves of group A
   __shared__ __attribute__((aligned(1024))) char smem[kRingStages * G::STAGE];
@@ -550,7 +557,9 @@ void attn_fwd_kernel(AttnArgs a) {
 
   WaveCtx<D, FP8> c;
   load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
-  const float dq = load_uniform(a.q_scale, hs * nqb + wq_lo / kQBlock);
+  // δQ: the wave's block scale (uniform), or this lane's query's own scale
+  const float dq = QM == kQmToken ? (qrow < n ? a.q_scale[row0 + qrow] : 0.f)
+                                  : load_uniform(a.q_scale, hs * nqb + wq_lo / kQBlock);
   const float* __restrict__ ksc = a.k_scale + hsk * nkb;
   c.m_run = -__builtin_inff();
   c.l_run = 0.f;
@@ -715,13 +724,15 @@ __global__ __launch_bounds__(kThreads) void qk_tiles_kernel(const int8_t* __rest
 void launch_attn(const AttnArgs& a, bool causal, bool fp8, hipStream_t st) {
   const int64_t blocks = (int64_t)a.g.B * a.g.H * ceil_div(a.g.N, kAttnRows);
   const dim3 grid((unsigned)blocks), block(kAttnThreads);
-  const bool sm = a.qb_slots != nullptr;
+  const int qm = a.qb_slots != nullptr ? kQmSmooth : a.q_per_token ? kQmToken : kQmBlock;
 #define SAGE_ATTN(DD, F8, CS)                                                                  \
   do {                                                                                         \
-    if (sm)                                                                                    \
-      hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS, true>), grid, block, 0, st, a);          \
+    if (qm == kQmSmooth)                                                                       \
+      hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS, kQmSmooth>), grid, block, 0, st, a);     \
+    else if (qm == kQmToken)                                                                   \
+      hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS, kQmToken>), grid, block, 0, st, a);      \
     else                                                                                       \
-      hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS, false>), grid, block, 0, st, a);         \
+      hipLaunchKernelGGL((attn_fwd_kernel<DD, F8, CS, kQmBlock>), grid, block, 0, st, a);      \
   } while (0)
   if (a.g.d == 128) {
     if (!fp8) { if (causal) SAGE_ATTN(128, false, true); else SAGE_ATTN(128, false, false); }

@@ -224,6 +224,61 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------
+// Per-token INT8 of Q (dtcms summary, "SageAttention（v1）": per-token
+// quantisation of q; "SageAttention 2": finer granularity): the quantiser of
+// quant_block_kernel on each row alone.  D/8 threads share a row (16 bytes
+// each); a workgroup takes ROWS rows, all loads first.  scales[row0 + t] =
+// fp32(max|x|/127) · out_scale_mul, i.e. indexed like the token itself.
+// Grid (ceil(Nmax/ROWS), H, B).
+template <int D, int ROWS>
+__global__ __launch_bounds__(kThreads) void quant_row_kernel(const uint16_t* __restrict__ x16, SeqGeom g,
+                                                             float out_scale_mul, int8_t* __restrict__ codes,
+                                                             float* __restrict__ scales) {
+  constexpr int CG = D / 8, RPP = kThreads / CG, PASSES = ROWS / RPP;
+  static_assert(PASSES * RPP == ROWS, "rows must be a multiple of rows per pass");
+  const int b = blockIdx.z, h = blockIdx.y;
+  int64_t row0;
+  int n;
+  hs_rows(g, b, h, row0, n);
+  const int t0 = blockIdx.x * ROWS;
+  if (t0 >= n) return;
+  const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
+  v4i raw[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + rr + p * RPP;
+    raw[p] = (t < n) ? *reinterpret_cast<const v4i*>(x16 + (row0 + t) * D + cg * 8) : v4i{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + rr + p * RPP;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = (uint32_t)raw[p][j];
+      x[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+      x[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+#pragma unroll
+    for (int o = 1; o < CG; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));  // the row's CG lanes
+    const float sc = amax / kInt8Max;
+    const float r = 1.0f / sc;
+    if (t < n) {
+      uint2 w = {0u, 0u};  // an all-zero row (scale 0) has all codes 0
+      if (sc > 0.f) {
+        w.x = pack4_i8(int8_code(x[0], sc, r), int8_code(x[1], sc, r), int8_code(x[2], sc, r), int8_code(x[3], sc, r));
+        w.y = pack4_i8(int8_code(x[4], sc, r), int8_code(x[5], sc, r), int8_code(x[6], sc, r), int8_code(x[7], sc, r));
+      }
+      *reinterpret_cast<uint2*>(codes + (row0 + t) * D + cg * 8) = w;
+      if (cg == 0) scales[row0 + t] = sc * out_scale_mul;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // V per-channel absolute maximum (as fp32 bits; non-negative floats order like
 // their bit patterns, so an integer atomic max is exact).
 template <int D>
@@ -384,6 +439,7 @@ __global__ __launch_bounds__(kThreads) void v_prepare_kernel(const uint16_t* __r
 // ---------------------------------------------------------------------------
 // Host-side launchers.
 static inline dim3 hs_grid(const SeqGeom& g, int rows) { return dim3(ceil_div(g.N, rows), g.H, g.B); }
+constexpr int kRowsPerBlock = 64;  // rows per workgroup of the per-token quantiser
 
 void launch_zero(void* p, size_t bytes, hipStream_t st) {
   const int64_t n16 = (int64_t)(bytes / 16);
@@ -394,9 +450,10 @@ void launch_zero(void* p, size_t bytes, hipStream_t st) {
 
 void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, float sm_scale,
                      int8_t* q_int8, int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean,
-                     float* q_mean, long long* colsum, hipStream_t st) {
+                     float* q_mean, bool q_per_token, long long* colsum, hipStream_t st) {
   // gq: Q's geometry (H query heads); gk: K's (its own head count), same
-  // sequences.  q_mean != nullptr selects Q smoothing.
+  // sequences.  q_mean != nullptr selects Q smoothing, q_per_token per-token
+  // Q scales (not both).
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
   const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
   launch_zero(colsum, sizeof(long long) * (size_t)gk.B * gk.H * gk.d, st);
@@ -409,6 +466,9 @@ void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const 
     if (q_mean)                                                                                                \
       hipLaunchKernelGGL((quant_block_kernel<DD, kQBlock, kShiftBlock>), gqb, blk, 0, st, q16, gq,             \
                          (const long long*)nullptr, sm_scale, q_int8, q_scale, q_mean);                        \
+    else if (q_per_token)                                                                                      \
+      hipLaunchKernelGGL((quant_row_kernel<DD, kRowsPerBlock>), hs_grid(gq, kRowsPerBlock), blk, 0, st, q16,   \
+                         gq, sm_scale, q_int8, q_scale);                                                       \
     else                                                                                                       \
       hipLaunchKernelGGL((quant_block_kernel<DD, kQBlock, kShiftNone>), gqb, blk, 0, st, q16, gq,              \
                          (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);               \

@@ -9,7 +9,7 @@ namespace sage {
 struct AttnArgs {
   const int8_t* q;         // Q codes, same layout as the fp16 input
   const int8_t* k;         // K codes (H / kv_group heads)
-  const float* q_scale;    // [B][H][nqb], softmax scale folded in
+  const float* q_scale;    // [B][H][nqb] (per token: indexed like the Q rows), softmax scale folded in
   const float* k_scale;    // [B][Hkv][nkb]
   const uint8_t* v_packed; // packed V tiles (fp16 or e4m3), Hkv heads
   const float* v_scale;    // [B][Hkv][d] (FP8 mode)
@@ -23,6 +23,7 @@ struct AttnArgs {
   const int32_t* qb_slots = nullptr;
   const float* qb_fix = nullptr;
   const int32_t* qb_flags = nullptr;
+  bool q_per_token = false;  // q_scale holds one scale per query row
 };
 
 // Inputs and outputs of the Q-smoothing term kernel (smooth_q.hip).
@@ -44,7 +45,7 @@ struct QBiasArgs {
 void launch_zero(void* p, size_t bytes, hipStream_t st);
 void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, float sm_scale,
                      int8_t* q_int8, int8_t* k_int8, float* q_scale, float* k_scale, float* k_mean,
-                     float* q_mean, long long* colsum, hipStream_t st);
+                     float* q_mean, bool q_per_token, long long* colsum, hipStream_t st);
 void launch_q_bias(const QBiasArgs& a, hipStream_t st);
 void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st);
 void launch_v_prepare(const SeqGeom& g, const void* v, const float* v_scale, bool fp8, bool rowmajor,

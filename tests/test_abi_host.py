@@ -69,6 +69,11 @@ def test_workspace_sizes():
     assert so[9] - so[8] == so[10] - so[9] == 2 * 2 * 256 * 4
     assert so[11] - so[10] == 256 * ((2 * 2 * 8 * 4 + 255) // 256)
     assert sage.sage_attn_varlen_workspace_size(3, 200, 271, 2, 128, "fp16", smooth_q=True) > wv
+    # per-token Q scales: q_scale [B,H,N] instead of [B,H,ceil(N/128)]
+    to = sage.sage_test_workspace_layout(False, 1, 2, 256, 0, 64, "fp8", q_per_token=True)
+    assert to[3] - to[2] == 256 * ((2 * 256 * 4 + 255) // 256)
+    assert offs[3] - offs[2] == 256
+    assert sage.sage_attn_workspace_size(1, 2, 256, 64, "fp8", smooth_q=True, q_per_token=True) == 0
     # grouped K/V heads shrink every K/V region; invalid groupings give 0
     g = sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16", H_kv=1)
     assert 0 < g < sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16")
@@ -112,6 +117,8 @@ def _fwd(**over):
     (dict(lse=ALIGNED * 4 + 2), INVALID),    # lse misaligned
     (dict(lse=ALIGNED * 4), INVALID),        # lse overlaps the output
     (dict(smooth=1, d=96), INVALID),
+    (dict(smooth=4), INVALID),               # unknown option bit
+    (dict(smooth=3), UNSUPPORTED),           # Q smoothing with per-token Q scales
     (dict(smooth=1, wsb=sage.sage_attn_workspace_size(1, 2, 256, 64, "fp16")), WS_SMALL),  # needs more room
 ])
 def test_attn_fwd_rejects(over, status):
@@ -141,15 +148,16 @@ def test_varlen_rejects():
 
 def test_quant_rejects():
     L = sage.lib()
-    st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, None, ALIGNED * 3, ALIGNED * 4,
-                         ALIGNED * 5, ALIGNED * 6, None, ALIGNED * 8, 1 << 20, None)
-    assert st == INVALID
-    st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, ALIGNED * 9, ALIGNED * 3,
-                         ALIGNED * 4, ALIGNED * 5, ALIGNED * 6, None, ALIGNED * 8, 8, None)
-    assert st == WS_SMALL
-    st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, ALIGNED * 9, ALIGNED * 3,
-                         ALIGNED * 4, ALIGNED * 5, ALIGNED * 6, ALIGNED * 7 + 4, ALIGNED * 8, 1 << 20, None)
-    assert st == INVALID                            # q_mean misaligned
+    def quant(q_int8=ALIGNED * 9, q_mean=None, options=0, wsb=1 << 20):
+        return L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, q_int8, ALIGNED * 3,
+                               ALIGNED * 4, ALIGNED * 5, ALIGNED * 6, q_mean, options, ALIGNED * 8, wsb, None)
+    assert quant(q_int8=None) == INVALID
+    assert quant(wsb=8) == WS_SMALL
+    assert quant(q_mean=ALIGNED * 7 + 4, options=1) == INVALID      # q_mean misaligned
+    assert quant(q_mean=ALIGNED * 7) == INVALID                     # q_mean without Q smoothing
+    assert quant(options=1) == INVALID                              # Q smoothing without q_mean
+    assert quant(q_mean=ALIGNED * 7, options=3) == UNSUPPORTED      # smoothing + per-token scales
+    assert quant(options=8) == INVALID                              # unknown option bit
     st = L.sage_quant_v_fp8(ALIGNED, 1, 2, 256, 100, 0, None, 0, ALIGNED * 2, ALIGNED * 3, None)
     assert st == INVALID
     st = L.sage_test_qk_tiles(ALIGNED, ALIGNED * 2, 1, 1, 128, 64, ALIGNED * 3, 0, ALIGNED * 4, None)
