@@ -50,7 +50,14 @@ Readings where the pages are silent (each listed in the design notes):
     part of the score it carries, sm_scale * q̄ · (k - km) with the smoothed K
     in fp32, is added back exactly (fp64) to every score of the block's rows;
   * per-token Q scales (optional, finer granularity): a Q "block" of one
-    token, the same quantiser on each row alone.
+    token, the same quantiser on each row alone;
+  * MXFP4 mode (optional, [DT] "SageAttention 3"): Q, smoothed K, P and V as
+    OCP microscaling FP4 — e2m1 elements in blocks of 32 with one
+    power-of-two (E8M0) scale each, the scale chosen as the smallest power of
+    two that fits the block maximum under e2m1's largest value 6 (no
+    saturation); blocks run along the contracted axis (channels for Q and K,
+    keys for P and V, 32-key blocks aligned within the sequence); P is first
+    normalised by the running max (level one), then microscaled (level two).
 """
 from __future__ import annotations
 
@@ -64,6 +71,8 @@ K_BLOCK = 64       # tokens per K quantisation block
 KV_TILE = 64       # keys per online-softmax step
 INT8_MAX = 127
 E4M3_MAX = 448.0
+E2M1_MAX = 6.0     # largest OCP FP4 (e2m1) value
+MX_BLOCK = 32      # elements per microscaling block
 FIXED_POINT_SHIFT = 24   # fp16 values are integer multiples of 2^-24
 
 __all__ = [
@@ -72,6 +81,8 @@ __all__ = [
     "e4m3_decode", "e4m3_encode", "quant_v_fp8", "quant_v_fp8_dense", "quant_v_fp8_varlen",
     "qk_int", "sage_attention_rows", "sdpa_fp64_rows", "head_views_dense",
     "head_views_varlen", "q_block_mean", "quant_q_smooth", "q_smooth_bias", "quant_q_per_token",
+    "E2M1_MAX", "MX_BLOCK", "e2m1_decode", "e2m1_encode", "mx_block_exponent", "mx_quantize",
+    "quant_mxfp4_qk", "quant_mxfp4_v", "mxfp4_decode", "mxfp4_attention_rows",
 ]
 
 
@@ -359,6 +370,159 @@ def quant_v_fp8_varlen(v: np.ndarray, cu_seqlens: Sequence[int]):
             codes[:, a:b] = c
             scales[i] = s
     return codes, scales
+
+
+# ----------------------------------------------------------------------------
+# OCP FP4 (e2m1) and microscaling (MX) blocks ([DT] "SageAttention 3":
+# microscaling FP4 attention with two-level quantisation).  e2m1: 1 sign bit,
+# 2 exponent bits with bias 1, 1 mantissa bit, exponent field 0 subnormal
+# (spacing 0.5); magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6; no inf or NaN.
+# ----------------------------------------------------------------------------
+def e2m1_decode(codes: np.ndarray) -> np.ndarray:
+    """4-bit e2m1 codes (low nibble of each byte) -> fp64 values."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    e = (c >> 1) & 0x3
+    m = c & 0x1
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int64)))
+    return np.where(c & 0x8, -mag, mag)
+
+
+def e2m1_encode(x: np.ndarray) -> np.ndarray:
+    """Nearest e2m1 value, ties to the even mantissa, saturating at ±6; the
+    sign bit follows x (a negative value that rounds to zero gives -0)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E2M1_MAX)
+    # spacing of the binade: 0.5 below 2, 1 in [2, 4), 2 in [4, 6]
+    q = np.where(a < 2.0, 0.5, np.where(a < 4.0, 1.0, 2.0))
+    k = np.rint(a / q)                      # ties to even multiple = even mantissa
+    v = np.minimum(k * q, E2M1_MAX)
+    # value -> code: exponent field and mantissa bit of v
+    code = np.select([v == 0, v == 0.5, v == 1, v == 1.5, v == 2, v == 3, v == 4],
+                     [0, 1, 2, 3, 4, 5, 6], 7)
+    code = np.where(np.signbit(x), code | 0x8, code)   # the sign is kept, -0 included
+    return code.astype(np.uint8)
+
+
+def mx_block_exponent(amax: np.ndarray) -> np.ndarray:
+    """Smallest integer X with amax <= 6·2^X (the block maximum fits e2m1's
+    largest value), within E8M0's [-127, 127]; amax = 0 gives -127.  Exact:
+    with amax = f·2^e, f in [0.5, 1), X = e - 3 + (f > 0.75)."""
+    amax = np.asarray(amax, dtype=np.float64)
+    f, e = np.frexp(amax)
+    X = e.astype(np.int64) - 3 + (f > 0.75)
+    return np.where(amax > 0, np.clip(X, -127, 127), -127).astype(np.int64)
+
+
+def mx_quantize(x: np.ndarray, axis: int):
+    """MX FP4 of fp32 x in blocks of 32 along ``axis`` (the last block may be
+    partial): per block X = mx_block_exponent(max|x|), codes = e2m1(x / 2^X)
+    (an exact scaling).  Returns (codes uint8, same shape as x; X int64 with
+    ``axis`` replaced by the block count)."""
+    x = np.moveaxis(np.asarray(x, dtype=np.float32), axis, -1).astype(np.float64)
+    *lead, n = x.shape
+    nb = -(-n // MX_BLOCK)
+    xp = np.zeros((*lead, nb * MX_BLOCK))
+    xp[..., :n] = x
+    xb = xp.reshape(*lead, nb, MX_BLOCK)
+    X = mx_block_exponent(np.abs(xb).max(axis=-1))
+    codes = e2m1_encode(xb * np.ldexp(1.0, -X)[..., None]).reshape(*lead, nb * MX_BLOCK)[..., :n]
+    return np.moveaxis(codes, -1, axis), np.moveaxis(X, -1, axis)
+
+
+def mxfp4_decode(codes: np.ndarray, X: np.ndarray, axis: int) -> np.ndarray:
+    """Values of MX FP4 data: e2m1(code) · 2^X of its block (fp64)."""
+    c = np.moveaxis(e2m1_decode(codes), axis, -1)
+    sc = np.repeat(np.ldexp(1.0, np.moveaxis(X, axis, -1)), MX_BLOCK, axis=-1)[..., :c.shape[-1]]
+    return np.moveaxis(c * sc, -1, axis)
+
+
+def quant_mxfp4_qk(q: np.ndarray, k: np.ndarray):
+    """Q and the smoothed K as MX FP4 along channels (32-channel blocks of each
+    token).  Returns (q_codes, q_X [..., n, d/32], k_codes, k_X, k_mean); the
+    softmax scale stays outside (a power-of-two scale cannot hold it)."""
+    qc, qx = mx_quantize(q.astype(np.float32), -1)
+    km = k_token_mean(k)
+    kc, kx = mx_quantize(smooth_k(k, km), -1)
+    return qc, qx, kc, kx, km
+
+
+def quant_mxfp4_v(v: np.ndarray):
+    """V as MX FP4 along keys: per channel, blocks of 32 consecutive keys of
+    the sequence.  Returns (codes [..., n, d], X [..., ceil(n/32), d])."""
+    return mx_quantize(v.astype(np.float32), -2)
+
+
+def mxfp4_attention_rows(q_codes, q_X, k_codes, k_X, v_codes, v_X, rows: Sequence[int], causal: bool,
+                         sm_scale: float, tile: int = KV_TILE, score_eps: Optional[np.ndarray] = None,
+                         score_bias: Optional[np.ndarray] = None):
+    """Output rows of the MXFP4 attention for one (sequence, head).
+
+    S = (Q̃ K̃ᵀ)·sm_scale with Q̃, K̃ the decoded MX FP4 values; online softmax
+    over 64-key tiles in ascending order (exact per-tile max, [IP] §3.1);
+    level one: p = e^(s - m) <= 1; level two: per query and 32-key block,
+    p̃ = e2m1(p / 2^X)·2^X with X from the block's largest p; O = αO + P̃·Ṽ;
+    out = fp16(O / l), l from the unrounded p.  fp64 arithmetic.
+
+    ``score_eps`` [n] (natural-log units, per key): as for the fp8 path, the
+    P codes (and block exponents) a score moved by at most ε may take are
+    left open; then (out, bound) is returned, bound fp64 [len(rows), d].
+    ``score_bias`` [ceil(n/128), n]: a term added to the scores of each Q
+    block's rows, as in ``sage_attention_rows``.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    n, d = k_codes.shape
+    R = len(rows)
+    qv = mxfp4_decode(q_codes[rows], q_X[rows], -1)
+    kv = mxfp4_decode(k_codes, k_X, -1)
+    vv = mxfp4_decode(v_codes, v_X, -2)
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
+    O = np.zeros((R, d))
+    W = np.zeros((R, d))
+    Wabs = np.zeros((R, d))
+    last_row = int(rows.max()) if R else -1
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        for t0 in range(0, n, tile):
+            if causal and t0 > last_row:
+                break
+            keys = np.arange(t0, min(n, t0 + tile))
+            s = (qv @ kv[keys].T) * float(sm_scale)
+            if score_bias is not None:
+                s = s + score_bias[rows // Q_BLOCK][:, keys]
+            if causal:
+                s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+            m_new = np.maximum(m, s.max(axis=1))
+            live = m_new > -np.inf
+            alpha = np.where(live, np.exp(m - m_new), 1.0)
+            alpha = np.where(np.isneginf(m) & live, 0.0, alpha)
+            p = np.where(live[:, None], np.exp(s - m_new[:, None]), 0.0)
+            l = alpha * l + p.sum(axis=1)
+            pq = np.zeros_like(p)
+            dcode = np.zeros_like(p)
+            for b0 in range(0, len(keys), MX_BLOCK):       # 32-key blocks of the tile
+                sl = slice(b0, b0 + MX_BLOCK)
+                pb = p[:, sl]
+                X = mx_block_exponent(pb.max(axis=1))[:, None]
+                pq[:, sl] = e2m1_decode(e2m1_encode(pb * np.ldexp(1.0, -X))) * np.ldexp(1.0, X)
+                if score_eps is not None:
+                    e2 = 2.0 * score_eps[keys[sl]][None, :]
+                    cands = []
+                    for ps in (pb * np.exp(-e2), pb * np.exp(e2)):
+                        for Xc in (mx_block_exponent(ps.max(axis=1))[:, None],
+                                   mx_block_exponent((pb * np.exp(-e2)).max(axis=1))[:, None],
+                                   mx_block_exponent((pb * np.exp(e2)).max(axis=1))[:, None]):
+                            cands.append(e2m1_decode(e2m1_encode(ps * np.ldexp(1.0, -Xc))) * np.ldexp(1.0, Xc))
+                    dcode[:, sl] = np.max([np.abs(c - pq[:, sl]) for c in cands], axis=0)
+            O = alpha[:, None] * O + pq @ vv[keys]
+            if score_eps is not None:
+                W = alpha[:, None] * W + dcode @ np.abs(vv[keys])
+                Wabs = alpha[:, None] * Wabs + pq @ np.abs(vv[keys])
+            m = m_new
+    out = O / l[:, None]
+    if score_eps is not None:
+        gamma = np.expm1(4.0 * np.max(score_eps))
+        return out.astype(np.float16), (W + gamma * (W + 2.0 * Wabs)) / l[:, None]
+    return out.astype(np.float16)
 
 
 # ----------------------------------------------------------------------------

@@ -716,3 +716,116 @@ def test_q_per_token_varlen_equals_per_sequence_dense():
         assert (quant["q_scale"][:, a:b] == dense["q_scale"][0]).all()
         qi, qs, _, _ = O.head_views_varlen(quant, cu, i, 1)
         assert (qs == dense["q_scale"][0, 1]).all()
+
+
+# --------------------------------------------------------------------------
+# MXFP4
+# --------------------------------------------------------------------------
+def test_e2m1_from_format_definition():
+    """Decode: the sixteen codes of 1 sign, 2 exponent (bias 1), 1 mantissa
+    bit; encode: brute-force nearest value with ties to the even mantissa,
+    saturation at 6, sign kept."""
+    want = [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert O.e2m1_decode(np.arange(8)).tolist() == want
+    assert O.e2m1_decode(np.arange(8, 16)).tolist() == [-w for w in want]
+    assert (O.e2m1_encode(O.e2m1_decode(np.arange(16))) == np.arange(16)).all()
+    rng = np.random.default_rng(81)
+    x = np.concatenate([rng.uniform(-8, 8, 4000), np.arange(-7, 7.25, 0.25), [1e-9, -1e-9, 100.0, -100.0]])
+    got = O.e2m1_encode(x)
+    mags = np.array(want)
+    for xi, ci in zip(x, got):
+        a = min(abs(xi), 6.0)
+        dist = np.abs(mags - a)
+        best = np.flatnonzero(dist == dist.min())
+        c = best[0] if len(best) == 1 else best[best % 2 == 0][0]   # even code = even mantissa
+        assert ci == (c | (8 if xi < 0 else 0)), (xi, ci, c)
+
+
+def test_mx_block_exponent_brute_force():
+    rng = np.random.default_rng(82)
+    a = np.concatenate([np.exp2(rng.uniform(-30, 30, 3000)), 6.0 * np.exp2(np.arange(-20, 20)),
+                        0.75 * np.exp2(np.arange(-20, 20)), [0.0]])
+    X = O.mx_block_exponent(a)
+    for ai, xi in zip(a, X):
+        if ai == 0:
+            assert xi == -127
+            continue
+        cand = [x for x in range(-127, 128) if ai <= 6.0 * 2.0 ** x]
+        assert xi == cand[0], (ai, xi)
+
+
+def test_mx_quantize_blocks_and_bounds():
+    """Blocks of 32 along the chosen axis (last partial), never saturated, each
+    element within half a step of its block's grid; the block maximum lands in
+    (3, 6]·2^X."""
+    rng = np.random.default_rng(83)
+    x = (rng.standard_normal((70, 100)) * np.exp2(rng.integers(-8, 8, (70, 1)))).astype(np.float32)
+    for axis in (0, 1):
+        codes, X = O.mx_quantize(x, axis)
+        vals = O.mxfp4_decode(codes, X, axis)
+        n = x.shape[axis]
+        assert X.shape[axis] == -(-n // 32)
+        xb = np.moveaxis(x, axis, -1).astype(np.float64)
+        vb = np.moveaxis(vals, axis, -1)
+        Xb = np.moveaxis(X, axis, -1)
+        for j in range(Xb.shape[-1]):
+            blk = xb[:, 32 * j:32 * j + 32]
+            sc = np.ldexp(1.0, Xb[:, j])[:, None]
+            amax = np.abs(blk).max(axis=1)
+            assert ((amax <= 6 * sc[:, 0]) & (amax > 3 * sc[:, 0])).all()
+            step = np.where(np.abs(blk) / sc < 2, 0.5, np.where(np.abs(blk) / sc < 4, 1.0, 2.0)) * sc
+            assert (np.abs(vb[:, 32 * j:32 * j + 32] - blk) <= step / 2 + 1e-300).all()
+
+
+def test_mxfp4_attention_special_cases():
+    """One visible key: the decoded V row; Q = 0: the mean of the decoded
+    visible V rows (every p is 1, exactly representable); and with P and V
+    taken exact (no MX step on them), Q and K on an exact MX grid give exact
+    attention."""
+    rng = np.random.default_rng(84)
+    n, d = 150, 64
+    q = rng.standard_normal((n, d)).astype(np.float16)
+    k = (rng.standard_normal((n, d)) + 2 * rng.standard_normal(d)).astype(np.float16)
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    qc, qx, kc, kx, km = O.quant_mxfp4_qk(q, k)
+    vc, vx = O.quant_mxfp4_v(v)
+    vv = O.mxfp4_decode(vc, vx, 0)
+    sm = float(O.default_sm_scale(d))
+    o = O.mxfp4_attention_rows(qc, qx, kc, kx, vc, vx, [0], True, sm)
+    assert (o[0] == vv[0].astype(np.float16)).all()
+    zc, zx, _, _, _ = O.quant_mxfp4_qk(np.zeros_like(q), k)
+    o = O.mxfp4_attention_rows(zc, zx, kc, kx, vc, vx, np.arange(n), True, sm)
+    want = np.cumsum(vv, axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.abs(o - want).max() <= 2 ** -10 * (1 + np.abs(want).max())
+    o = O.mxfp4_attention_rows(zc, zx, kc, kx, vc, vx, np.arange(n), False, sm)
+    assert np.abs(o - vv.mean(axis=0)).max() <= 2 ** -10 * (1 + np.abs(vv).max())
+
+
+def test_mxfp4_close_to_exact_attention_and_envelope():
+    """Against fp64 exact attention the MXFP4 method keeps cos >= 0.95 on
+    Gaussian inputs with a K bias (FP4's 3-bit elements; a reported property,
+    not the 99.8 % bar), and the open-code bound covers scores moved by up to
+    ε (random per-key perturbations that move codes and block exponents)."""
+    x = workloads.generate_custom(85, 1, 1, 300, 64, k_bias=3.0)
+    q, k, v = x.q[0, 0], x.k[0, 0], x.v[0, 0]
+    qc, qx, kc, kx, km = O.quant_mxfp4_qk(q, k)
+    vc, vx = O.quant_mxfp4_v(v)
+    sm = float(O.default_sm_scale(64))
+    rows = np.arange(300)
+    rng = np.random.default_rng(86)
+    for causal in (False, True):
+        base = O.mxfp4_attention_rows(qc, qx, kc, kx, vc, vx, rows, causal, sm)
+        ref = O.sdpa_fp64_rows(q, k, v, rows, causal)
+        assert cos(base, ref) >= 0.95
+        eps = np.full(300, 1e-3)
+        b2, W = O.mxfp4_attention_rows(qc, qx, kc, kx, vc, vx, rows, causal, sm, score_eps=eps)
+        assert (b2 == base).all() and W.max() > 0
+        moved = 0
+        for trial in range(6):
+            pert = np.tile(rng.uniform(-1, 1, 300) * eps, (3, 1))
+            o = O.mxfp4_attention_rows(qc, qx, kc, kx, vc, vx, rows, causal, sm, score_bias=pert)
+            diff = np.abs(o.astype(np.float64) - base.astype(np.float64))
+            slack = 2 ** -10 * np.abs(base.astype(np.float64)) + 1e-6
+            assert (diff <= W + slack).all(), (causal, trial, (diff - W - slack).max())
+            moved += int((diff > slack).sum())
+        assert moved > 0
