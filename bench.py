@@ -14,6 +14,7 @@ HBM.  Prints ONE JSON line:
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -26,6 +27,7 @@ sys.path.insert(0, ROOT)
 INT8_PEAK_TOPS = 5000.0      # MI355X dense INT8 MFMA
 FP16_PEAK_TFLOPS = 2500.0    # MI355X dense FP16 MFMA
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+FP4_PEAK_TFLOPS = 10100.0    # MI355X dense FP4 (MXFP4) MFMA
 HBM_PEAK_GBS = 8000.0
 DEFAULT_WORKLOAD = "seq16k"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic.json")
@@ -45,7 +47,10 @@ def attn_ops(w, lengths=None):
 
 
 def path_ceiling(pv_mode):
-    """Half of the ops are the INT8 QKᵀ, half the PV product at its own rate."""
+    """Half of the ops are the QKᵀ product (INT8, or FP4 in MXFP4 mode), half the
+    PV product, each at its own rate."""
+    if pv_mode == "mxfp4":
+        return FP4_PEAK_TFLOPS
     pv_peak = FP8_PEAK_TFLOPS if pv_mode == "fp8" else FP16_PEAK_TFLOPS
     return 1.0 / (0.5 / INT8_PEAK_TOPS + 0.5 / pv_peak)
 
@@ -214,6 +219,9 @@ def main():
     ap.add_argument("--smooth-q", action="store_true",
                     help="time the forward with Q smoothing (the score term of Q's block mean added back)")
     ap.add_argument("--q-per-token", action="store_true", help="time the forward with per-token Q scales")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="time the forward in MXFP4 mode (QK and PV in microscaling FP4) instead of the "
+                         "workload's PV mode")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (calibrates the HBM byte counters)")
     ap.add_argument("--rocprof-summary", nargs="+", metavar="DB",
@@ -251,6 +259,8 @@ def main():
         return
 
     w = workloads.get(args.workload)
+    if args.mxfp4:
+        w = dataclasses.replace(w, pv_mode="mxfp4")
     sq, qt = bool(args.smooth_q), bool(args.q_per_token)
     opts = dict(smooth_q=sq, q_per_token=qt)
     log(f"bench: workload {w.name}: {w.description}" + (" (Q smoothing)" if sq else "") +
@@ -309,7 +319,7 @@ def main():
         traffic = measured_traffic(w.name + ("+smooth_q" if sq else "") + ("+q_per_token" if qt else ""))
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
-                    "kernel": f"attn_fwd_kernel<{w.d},{'fp8' if w.pv_mode == 'fp8' else 'fp16'}"
+                    "kernel": f"{'attn_mx_kernel' if w.pv_mode == 'mxfp4' else 'attn_fwd_kernel'}<{w.d},{w.pv_mode}"
                               f"{',smooth_q' if sq else ''}{',q_per_token' if qt else ''}>",
                     "kernel_ms": round(kern_ms, 4),
                     "path_ceiling": round(path_ceiling(w.pv_mode), 1),
@@ -319,7 +329,7 @@ def main():
             f"({100 * achieved / INT8_PEAK_TOPS:.1f}% of INT8 peak)")
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.pv_mode != "mxfp4" and not (sq or qt):
         log("bench: timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(w, x)
 
@@ -338,7 +348,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8 QK / fp8 PV" if w.pv_mode == "fp8" else "int8 QK / fp16 PV",
+        "dtype": {"fp8": "int8 QK / fp8 PV", "mxfp4": "mxfp4 QK / mxfp4 PV"}.get(w.pv_mode, "int8 QK / fp16 PV"),
         "data": "synthetic",
         "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
         "config": config,

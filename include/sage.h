@@ -66,7 +66,15 @@ typedef enum {
   SAGE_ERR_DEVICE = 4
 } sage_status_t;
 
-typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1 } sage_pv_mode_t;
+/* SAGE_MXFP4: QKᵀ and PV both in OCP microscaling FP4 (dtcms summary, section
+ * "SageAttention 3": microscaling FP4 attention, two-level quantisation):
+ * e2m1 elements in blocks of 32 along the contracted axis (channels for Q and
+ * the smoothed K, keys for P and V) with one E8M0 power-of-two scale each, the
+ * smallest under which the block maximum fits e2m1's largest value 6; P is the
+ * online softmax's p = e^(s - m) <= 1 (level one) microscaled per 32-key block
+ * (level two).  Takes no options.  Far coarser than the INT8 path (3-bit
+ * elements): about 0.97 cosine to exact attention on Gaussian inputs. */
+typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1, SAGE_MXFP4 = 2 } sage_pv_mode_t;
 
 /* Options, OR-ed into the `options` argument (0 = the default method).
  *   SAGE_OPT_SMOOTH_Q: Q smoothing — each 128-token Q block's channel mean q̄
@@ -149,7 +157,8 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
  *   (smoothed K: exact attention shifted by the row constant q·km·sm_scale),
  *   for merging partial results over key ranges; 4-byte aligned, no overlap.
  *   is_causal != 0 masks key j > query i (deepseek.csdn.net post: is_causal).
- *   pv_mode selects FP16 PV or FP8-e4m3 PV.  options (sage_option_t bits):
+ *   pv_mode selects FP16 PV, FP8-e4m3 PV, or SAGE_MXFP4 (QKᵀ and PV in MXFP4;
+ *   options must be 0, else SAGE_ERR_UNSUPPORTED).  options (sage_option_t bits):
  *   SAGE_OPT_SMOOTH_Q — Q̂ and δQ come from Q minus its block mean and every
  *   score of a row of block b gets sm_scale·q̄_b·(k_j − km) added back
  *   (carried within one unit of δQ·δK; the workspace is then larger);
@@ -204,6 +213,13 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  *   fp32 — then [9] holds it, as sm_scale·q̄_b·x_j·log2(e) — else [8] holds
  *   1.5·2^23 bits + rint(that / (δQ_b·δK_t·log2 e))), [11] total size
  *   (internal scratch sits between [6] and [7]).
+ *   With SAGE_MXFP4 the regions are instead [0] Q e2m1 codes [rows][d/2]
+ *   (channel c in nibble c%2 of byte c/2), [1] the smoothed K's codes, [2] Q
+ *   E8M0 scale bytes [rows][8] (byte 4g + kk: channel block 2kk + g), [3] per
+ *   K/V tile 1 KB of scales (K: 8 bytes per key in the kernel's row order;
+ *   V: at 512 + 4·lane + dt), [4] k_mean, [5] packed V codes per tile
+ *   ([dt][lane] 16 bytes: channel 32dt + lane%32, keys 32(lane/32) + j in
+ *   nibble j), [6]-[10] empty.
  *   For dense calls pass B,H,H_kv,N,d (total_tokens ignored); for varlen pass
  *   B = nseq, N = max_seqlen and total_tokens.  offsets_out is HOST memory.
  *   The int8/scale/mean regions use the same layouts as sage_quant_qk, with
@@ -220,7 +236,8 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  *   workspace that a preceding sage_attn_fwd call with the same B,H,H_kv,N,d,
  *   is_causal, pv_mode and options has filled (its pre-pass results are reused as they
  *   are); writes o fp16 [B,H,N,d] (no LSE).  Used to time the attention
- *   kernel alone.  Same validation as sage_attn_fwd.
+ *   kernel alone.  Same validation as sage_attn_fwd.  SAGE_MXFP4 uses the
+ *   default softmax scale.
  */
 sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int N, int d,
                                             int is_causal, sage_pv_mode_t pv_mode, int options,

@@ -26,7 +26,7 @@ __all__ = [
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libsage.so")
-PV_MODES = {"fp16": 0, "fp8": 1}
+PV_MODES = {"fp16": 0, "fp8": 1, "mxfp4": 2}
 LAYOUT_HND = 0
 OPT_SMOOTH_Q = 1        # sage_option_t bits
 OPT_Q_PER_TOKEN = 2

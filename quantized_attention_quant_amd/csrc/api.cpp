@@ -38,13 +38,31 @@ struct WsLayout {
   size_t total;
 };
 
-WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d, bool fp8, int options) {
+WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d, sage_pv_mode_t pv_mode,
+                     int options) {
+  const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
   const bool smooth_q = (options & SAGE_OPT_SMOOTH_Q) != 0;
   const bool q_per_token = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
   const int64_t tokens = varlen ? (int64_t)H * T : (int64_t)B * H * N;
   const int64_t ktokens = varlen ? (int64_t)Hkv * T : (int64_t)B * Hkv * N;
   const int64_t nqb = ceil_div64(N, sage::kQBlock), nkb = ceil_div64(N, sage::kKBlock);
   const int64_t vtiles = varlen ? (int64_t)Hkv * sage::vtiles_per_head_varlen(T, B) : (int64_t)B * Hkv * nkb;
+  if (pv_mode == SAGE_MXFP4) {
+    // [0] Q e2m1 codes [1] K codes [2] Q scales (8 B per row) [3] per-tile
+    // K/V scales [4] k_mean [5] packed V codes [7] K column sums
+    const size_t sizes[kWsRegions] = {
+        (size_t)(tokens * d / 2), (size_t)(ktokens * d / 2), (size_t)tokens * 8,
+        (size_t)vtiles * sage::kMxAuxBytes, sizeof(float) * (size_t)B * Hkv * d,
+        (size_t)vtiles * sage::kKBlock * d / 2, 0, sizeof(long long) * (size_t)B * Hkv * d, 0, 0, 0, 0};
+    WsLayout L;
+    size_t cur = 0;
+    for (int i = 0; i < kWsRegions; ++i) {
+      L.off[i] = cur;
+      cur = align_up(cur + sizes[i]);
+    }
+    L.total = cur;
+    return L;
+  }
   const size_t qblocks = (size_t)B * H * nqb;  // (sequence, head, Q block) rows
   const size_t sq = smooth_q ? 1 : 0;
   const size_t sizes[kWsRegions] = {
@@ -78,6 +96,11 @@ constexpr int kKnownOptions = SAGE_OPT_SMOOTH_Q | SAGE_OPT_Q_PER_TOKEN;
 inline bool options_known(int o) { return (o & ~kKnownOptions) == 0; }
 // Q smoothing carries its term in units of a per-block δQ: not with per-token scales.
 inline bool options_supported(int o) { return (o & kKnownOptions) != kKnownOptions; }
+inline bool pv_mode_ok(sage_pv_mode_t m) { return m == SAGE_PV_FP16 || m == SAGE_PV_FP8_E4M3 || m == SAGE_MXFP4; }
+// MXFP4 has its own Q scales (E8M0 per 32 channels): no Q smoothing or per-token option.
+inline bool mode_options_supported(sage_pv_mode_t m, int o) {
+  return options_supported(o) && (m != SAGE_MXFP4 || o == 0);
+}
 
 sage_status_t check_dims(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1) return SAGE_ERR_INVALID_ARGUMENT;
@@ -121,15 +144,15 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SAGE_ERR_INVALID_ARGUMENT;
   if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return SAGE_ERR_INVALID_ARGUMENT;
   if ((reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0) return SAGE_ERR_INVALID_ARGUMENT;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!pv_mode_ok(pv_mode)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!options_supported(options)) return SAGE_ERR_UNSUPPORTED;
+  if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
   float sm;
   if (!resolve_sm_scale(sm_scale, g.d, &sm)) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
   const bool sq = (options & SAGE_OPT_SMOOTH_Q) != 0;
   const bool qtok = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
-  const WsLayout L = make_layout(varlen, g.B, g.H, Hkv, g.N, g.T, g.d, fp8, options);
+  const WsLayout L = make_layout(varlen, g.B, g.H, Hkv, g.N, g.T, g.d, pv_mode, options);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const int64_t rows = varlen ? (int64_t)g.H * g.T : (int64_t)g.B * g.H * g.N;
   const size_t tensor_bytes = (size_t)rows * g.d * 2;
@@ -146,6 +169,21 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   char* ws = static_cast<char*>(workspace);
+  SeqGeom gk = g;
+  gk.H = Hkv;
+  if (pv_mode == SAGE_MXFP4) {
+    uint8_t* aux = reinterpret_cast<uint8_t*>(ws + L.off[3]);
+    sage::launch_zero(aux, L.off[4] - L.off[3], st);  // K scales of rows past a sequence's end stay 0
+    sage::launch_mx_prepare(g, gk, q, k, v, reinterpret_cast<uint8_t*>(ws + L.off[0]),
+                            reinterpret_cast<uint8_t*>(ws + L.off[2]), reinterpret_cast<uint8_t*>(ws + L.off[1]), aux,
+                            reinterpret_cast<uint8_t*>(ws + L.off[5]), reinterpret_cast<float*>(ws + L.off[4]),
+                            reinterpret_cast<long long*>(ws + L.off[7]), st);
+    const sage::MxArgs a{reinterpret_cast<const uint8_t*>(ws + L.off[0]), reinterpret_cast<const uint8_t*>(ws + L.off[2]),
+                         reinterpret_cast<const uint8_t*>(ws + L.off[1]), reinterpret_cast<const uint8_t*>(ws + L.off[5]),
+                         aux, static_cast<uint16_t*>(o), lse, g, g.H / Hkv, (float)((double)sm * 1.4426950408889634)};
+    sage::launch_attn_mx(a, is_causal != 0, st);
+    return finish(st);
+  }
   int8_t* q8 = reinterpret_cast<int8_t*>(ws + L.off[0]);
   int8_t* k8 = reinterpret_cast<int8_t*>(ws + L.off[1]);
   float* qs = reinterpret_cast<float*>(ws + L.off[2]);
@@ -159,8 +197,6 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   float* fix = reinterpret_cast<float*>(ws + L.off[10]);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.off[11]);
 
-  SeqGeom gk = g;
-  gk.H = Hkv;
   sage::launch_quant_qk(g, gk, q, k, sm, q8, k8, qs, ks, km, qm, qtok, colsum, st);
   if (sq) {
     const sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, ks, qm, qs, slots, fix, flags, g, g.H / Hkv,
@@ -269,9 +305,9 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
 
 size_t sage_attn_workspace_size(int B, int H, int H_kv, int N, int d, sage_pv_mode_t pv_mode, int options) {
   if (check_dims(B, H, N, d) != SAGE_OK || !kv_heads_ok(H, H_kv)) return 0;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
-  if (!options_known(options) || !options_supported(options)) return 0;
-  return make_layout(false, B, H, H_kv, N, 0, d, pv_mode == SAGE_PV_FP8_E4M3, options).total;
+  if (!pv_mode_ok(pv_mode)) return 0;
+  if (!options_known(options) || !mode_options_supported(pv_mode, options)) return 0;
+  return make_layout(false, B, H, H_kv, N, 0, d, pv_mode, options).total;
 }
 
 sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -290,9 +326,9 @@ size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_t
                                        sage_pv_mode_t pv_mode, int options) {
   if (nseq < 1 || total_tokens < 0 || check_dims(nseq, H, max_seqlen, d) != SAGE_OK || !kv_heads_ok(H, H_kv))
     return 0;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return 0;
-  if (!options_known(options) || !options_supported(options)) return 0;
-  return make_layout(true, nseq, H, H_kv, max_seqlen, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3, options).total;
+  if (!pv_mode_ok(pv_mode)) return 0;
+  if (!options_known(options) || !mode_options_supported(pv_mode, options)) return 0;
+  return make_layout(true, nseq, H, H_kv, max_seqlen, total_tokens, d, pv_mode, options).total;
 }
 
 sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -310,11 +346,11 @@ sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int
                                          sage_pv_mode_t pv_mode, int options, size_t offsets_out[12]) {
   if (!offsets_out) return SAGE_ERR_INVALID_ARGUMENT;
   if (check_dims(B, H, N, d) != SAGE_OK || !kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!pv_mode_ok(pv_mode)) return SAGE_ERR_INVALID_ARGUMENT;
   if (varlen && total_tokens < 0) return SAGE_ERR_INVALID_ARGUMENT;
   if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!options_supported(options)) return SAGE_ERR_UNSUPPORTED;
-  const WsLayout L = make_layout(varlen != 0, B, H, H_kv, N, total_tokens, d, pv_mode == SAGE_PV_FP8_E4M3, options);
+  if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
+  const WsLayout L = make_layout(varlen != 0, B, H, H_kv, N, total_tokens, d, pv_mode, options);
   for (int i = 0; i < 7; ++i) offsets_out[i] = L.off[i];
   for (int i = 8; i < kWsRegions; ++i) offsets_out[i - 1] = L.off[i];
   offsets_out[11] = L.total;
@@ -329,16 +365,26 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
   if (!kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!o || !workspace || !aligned16(o) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
     return SAGE_ERR_INVALID_ARGUMENT;
-  if (pv_mode != SAGE_PV_FP16 && pv_mode != SAGE_PV_FP8_E4M3) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!pv_mode_ok(pv_mode)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!options_supported(options)) return SAGE_ERR_UNSUPPORTED;
+  if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
-  const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, fp8, options);
+  const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, pv_mode, options);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const size_t tensor_bytes = (size_t)B * H * N * d * 2;
   if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
   const char* ws = static_cast<const char*>(workspace);
   const SeqGeom g{nullptr, B, H, N, d, 0};
+  if (pv_mode == SAGE_MXFP4) {
+    float sm;
+    resolve_sm_scale(0.f, d, &sm);
+    const sage::MxArgs a{reinterpret_cast<const uint8_t*>(ws + L.off[0]), reinterpret_cast<const uint8_t*>(ws + L.off[2]),
+                         reinterpret_cast<const uint8_t*>(ws + L.off[1]), reinterpret_cast<const uint8_t*>(ws + L.off[5]),
+                         reinterpret_cast<const uint8_t*>(ws + L.off[3]), static_cast<uint16_t*>(o), nullptr, g,
+                         H / H_kv, (float)((double)sm * 1.4426950408889634)};
+    sage::launch_attn_mx(a, is_causal != 0, reinterpret_cast<hipStream_t>(stream));
+    return finish(reinterpret_cast<hipStream_t>(stream));
+  }
   sage::AttnArgs a{reinterpret_cast<const int8_t*>(ws + L.off[0]), reinterpret_cast<const int8_t*>(ws + L.off[1]),
                    reinterpret_cast<const float*>(ws + L.off[2]), reinterpret_cast<const float*>(ws + L.off[3]),
                    reinterpret_cast<const uint8_t*>(ws + L.off[5]), reinterpret_cast<const float*>(ws + L.off[6]),

@@ -685,6 +685,340 @@ void attn_fwd_kernel(AttnArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// MXFP4 attention (dtcms summary, section "SageAttention 3": microscaling FP4
+// attention with two-level quantisation; operands prepared in quant.hip).
+// The schedule is attn_fwd_kernel's (two wave groups, one barrier per tile,
+// LDS DMA two tiles ahead); what differs:
+//   * Sᵀ = K̂Q̂ᵀ and Oᵀ = VᵀPᵀ both run on v_mfma_scale_f32_32x32x64_f8f6f4 with
+//     e2m1 operands: each lane supplies 32 elements of one 32-wide block along
+//     the contraction and that block's E8M0 scale; the accumulator is fp32.
+//   * The K̂ rows of a tile sit in LDS in the order that makes each lane
+//     half's 32 scores the keys 32g .. 32g+31 of the tile, so a lane's P values
+//     are exactly one 32-key MX block of its query: level one is the online
+//     softmax's p = 2^(s - m) <= 1, level two the block's power-of-two scale
+//     from the lane's own largest p, then the hardware e2m1 conversion.
+//   * LDS stage: K̂ codes (rows of d/2 bytes, 16-byte chunks XOR-swizzled on
+//     the 256-byte bank line), packed V codes, and 1 KB of scales (K: 8 bytes
+//     per row; V: 4 bytes per lane).
+template <int D>
+struct MxGeom {
+  static constexpr int KBYTES = kKBlock * D / 2;  // K̂ codes of a tile
+  static constexpr int VBYTES = kKBlock * D / 2;  // packed V codes
+  static constexpr int STAGE = KBYTES + VBYTES + kMxAuxBytes;
+  static constexpr int KCH = KBYTES / 16;
+  static constexpr int CI = (KBYTES + VBYTES) / 16 / kThreads;  // 16-byte DMA instructions per group-A wave
+  static constexpr int CPR = D / 32;                             // 16-byte chunks per K̂ row
+  static constexpr int RSH = (D == 128) ? 2 : 3;                 // log2 of rows per 256-byte bank line
+  static_assert(CI * kThreads * 16 == KBYTES + VBYTES, "tile must split evenly over the waves");
+  static __device__ __forceinline__ int chunk(int r, int c) { return r * CPR + (c ^ ((r >> RSH) & (CPR - 1))); }
+};
+
+// Key of LDS row r of an MXFP4 K̂ tile: row 32s + 8q + 4g + t holds key
+// 32g + 16s + 4q + t.
+__device__ __forceinline__ int mx_key_of_row(int r) {
+  return 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
+}
+
+template <int D>
+__device__ __forceinline__ void issue_mx_tile(const void* kbase, int kbytes, const void* vbase, int vbytes,
+                                              const void* abase, int abytes, int t, char* stage, int w, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using G = MxGeom<D>;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), (short)0, kbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(vbase), (short)0, vbytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(abase), (short)0, abytes, kBufferFlags);
+#pragma unroll
+  for (int j = 0; j < G::CI; ++j) {
+    const int base = (w * G::CI + j) * 64;  // wave-uniform chunk index
+    if (base < G::KCH) {
+      // LDS slot p holds logical chunk (slot ^ swizzle) of row p / CPR
+      const int p = base + lane;
+      const int r = p / G::CPR, cs = p % G::CPR;
+      const int c = cs ^ ((r >> G::RSH) & (G::CPR - 1));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_ptr_t)(stage + base * 16), 16,
+                                               (t * kKBlock + mx_key_of_row(r)) * (D / 2) + c * 16, 0, 0, 0);
+    } else {
+      const int p = base - G::KCH;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + p * 16), 16,
+                                               t * G::VBYTES + (p + lane) * 16, 0, 0, 0);
+    }
+  }
+  // scales: wave w (< 4) brings bytes 256w .. 256w+255 of the tile's 1 KB
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + G::KBYTES + G::VBYTES + w * 256), 4,
+                                           t * kMxAuxBytes + w * 256 + lane * 4, 0, 0, 0);
+#endif
+}
+
+// One scaled e2m1 MFMA with constant byte selects for both scales.
+template <int SA, int SB>
+__device__ __forceinline__ v16f mx_mfma(const v4i& a, const v4i& b, const v16f& c, int sa, int sb) {
+  const v8i A = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+  const v8i B = {b[0], b[1], b[2], b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, c, 4, 4, SA, sa, SB, sb);
+}
+
+template <int D>
+struct MxWave {
+  v4i qf[D / 64];   // Q̂ e2m1 codes: query r32, channels 64kk + 32g .. +31
+  int qsc;          // its E8M0 scales, byte kk
+  v16f O[D / 32];
+  v16f S[2];        // Sᵀ of the current tile (fp32)
+  v4i pk;           // P codes of the previous tile (one 32-key block per lane)
+  int psc;          // their E8M0 scale (byte 0)
+  float m_run;
+  float l_run;
+};
+
+// Matrix phase: PV of the previous tile (its P in pk) and QKᵀ of this one.
+template <int D>
+__device__ __forceinline__ void mx_matrix(const char* __restrict__ kstage, const char* __restrict__ vstage,
+                                          const char* __restrict__ astage, const char* __restrict__ avstage,
+                                          int lane, int r32, int gg, MxWave<D>& c) {
+  using G = MxGeom<D>;
+  constexpr int DT = D / 32;
+  const v4i* lk = reinterpret_cast<const v4i*>(kstage);
+  v4i kf[2][D / 64];
+  int ks[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int r = 32 * s + r32;
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) kf[s][kk] = lk[G::chunk(r, 2 * kk + gg)];
+    ks[s] = *reinterpret_cast<const int*>(astage + r * 8 + 4 * gg);
+  }
+  const v4i* lv = reinterpret_cast<const v4i*>(vstage);
+  v4i vf[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) vf[dt] = lv[dt * 64 + lane];
+  const int vsc = *reinterpret_cast<const int*>(avstage + 512 + 4 * lane);
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    v16f acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    acc = mx_mfma<0, 0>(kf[s][0], c.qf[0], acc, ks[s], c.qsc);
+    if (D == 128) acc = mx_mfma<1, 1>(kf[s][D / 64 - 1], c.qf[D / 64 - 1], acc, ks[s], c.qsc);
+    c.S[s] = acc;
+  }
+  c.O[0] = mx_mfma<0, 0>(vf[0], c.pk, c.O[0], vsc, c.psc);
+  c.O[1] = mx_mfma<1, 0>(vf[1], c.pk, c.O[1], vsc, c.psc);
+  if (D == 128) {
+    c.O[DT - 2] = mx_mfma<2, 0>(vf[DT - 2], c.pk, c.O[DT - 2], vsc, c.psc);
+    c.O[DT - 1] = mx_mfma<3, 0>(vf[DT - 1], c.pk, c.O[DT - 1], vsc, c.psc);
+  }
+  // schedule: every LDS read first, then the MFMAs (each read has the earlier
+  // MFMAs to land behind)
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 64) + 2 + DT + 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 64) + DT, 0);
+}
+
+// Masking of a tile that is not fully visible, in place: lane half gg holds
+// keys k0 + 32gg + 16s + i in S[s][i].
+template <bool CAUSAL>
+__device__ __forceinline__ void mx_mask(v16f (&S)[2], int k0, int n, int qrow, int gg) {
+  const int lim = (CAUSAL ? min(n - 1, qrow) : n - 1) - k0 - 32 * gg;
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v = S[s][i];
+      S[s][i] = (16 * s + i <= lim) ? v : -__builtin_inff();
+    }
+}
+
+// Softmax phase of one tile (masked scores already -inf): exact per-tile max
+// (the P codes follow it), the MX P block of this lane, the row sum of the
+// unrounded p.
+template <int D>
+__device__ __forceinline__ void mx_softmax(MxWave<D>& c, float c2) {
+  float F[2][16];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float f = c.S[s][i];
+      F[s][i] = f;
+    }
+  float lmx = -__builtin_inff();
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) lmx = max3f(lmx, F[s][i], F[s][i + 1]);
+  const float mt = pair_max(lmx) * c2;
+  float m_new = __builtin_fmaxf(c.m_run, mt);
+  m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
+  const float alpha = __builtin_amdgcn_exp2f(c.m_run - m_new);
+  if (__any(alpha != 1.f)) rescale_o<D>(c.O, c.l_run, alpha);
+  c.m_run = m_new;
+  // level two: this lane's 32 p are one block; its scale from its largest p
+  const int X = mx_exponent(__builtin_amdgcn_exp2f(__builtin_fmaf(lmx, c2, -m_new)));
+  const float sc = __builtin_ldexpf(1.f, X);
+  // all exponentials first, then the sums and conversions: the transcendental
+  // results are not waited on right after they are issued
+  float p[4][8];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) p[q][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[q >> 1][8 * (q & 1) + j], c2, -m_new));
+  __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);   // the FMAs
+  __builtin_amdgcn_sched_group_barrier(0x400, 32, 0);   // the exponentials
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[q] += p[q][j];
+    w[q] = mx_pack8(p[q], sc);
+  }
+  const float lsum = (part[0] + part[1]) + (part[2] + part[3]);
+  c.pk = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+  c.psc = X + 127;
+  c.l_run += lsum;
+}
+
+template <int D, bool CAUSAL>
+__global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads),
+                          amdgpu_waves_per_eu(kAttnWavesPerSimd<D, false>, kAttnWavesPerSimd<D, false>)))
+void attn_mx_kernel(MxArgs a) {
+  constexpr int DT = D / 32;
+  using G = MxGeom<D>;
+  __shared__ __attribute__((aligned(1024))) char smem[kRingStages * G::STAGE];
+
+  const SeqGeom& g = a.g;
+  const int nwb = ceil_div(g.N, kAttnRows);
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int wb = nwb - 1 - logical % nwb;
+  const int hb = logical / nwb;
+  const int h = hb / g.B, b = hb % g.B;
+  int64_t row0;
+  int n;
+  hs_rows(g, b, h, row0, n);
+  const int q0 = wb * kAttnRows;
+  if (q0 >= n) return;
+
+  const int tid = threadIdx.x, lane = tid & 63, r32 = lane & 31, gg = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = w < kAttnWaves / 2;
+  const int wq_lo = q0 + 32 * w;
+  const int qrow = wq_lo + r32;
+  const int wq_hi = min(wq_lo + 31, n - 1);
+  const bool wave_rows = wq_lo < n;
+
+  SeqGeom gk = g;
+  gk.H = g.H / a.kv_group;
+  const int hk = h / a.kv_group;
+  int64_t krow0;
+  int kn;
+  hs_rows(gk, b, hk, krow0, kn);
+
+  const int kend = CAUSAL ? min(n, q0 + kAttnRows) : n;
+  const int ntiles = ceil_div(kend, kKBlock);
+  const int ntiles_seq = ceil_div(n, kKBlock);
+  const uint8_t* kbase = a.k + krow0 * (D / 2);
+  const int kbytes = n * (D / 2);
+  const int64_t tile0 = vtile_index(gk, b, hk, 0);
+  const uint8_t* vbase = a.v + tile0 * G::VBYTES;
+  const int vbytes = ntiles_seq * G::VBYTES;
+  const uint8_t* abase = a.aux + tile0 * kMxAuxBytes;
+  const int abytes = ntiles_seq * kMxAuxBytes;
+  constexpr int L = G::CI + 1;
+
+  MxWave<D> c;
+#pragma unroll
+  for (int kk = 0; kk < D / 64; ++kk)
+    c.qf[kk] = (qrow < n) ? *reinterpret_cast<const v4i*>(a.q + (row0 + qrow) * (D / 2) + 32 * kk + 16 * gg)
+                          : v4i{0, 0, 0, 0};
+  c.qsc = (qrow < n) ? *reinterpret_cast<const int*>(a.q_scale + (row0 + qrow) * 8 + 4 * gg) : 0;
+  c.m_run = -__builtin_inff();
+  c.l_run = 0.f;
+  c.pk = v4i{0, 0, 0, 0};
+  c.psc = 0;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c.O[dt][i] = 0.f;
+
+  if (lead) {
+    const int first = min(kAhead, ntiles);
+    for (int t = 0; t < first; ++t)
+      issue_mx_tile<D>(kbase, kbytes, vbase, vbytes, abase, abytes, t, smem + t * G::STAGE, w, lane);
+  }
+  wait_dma<0>();
+  barrier_only();
+
+  const int nact = !wave_rows ? 0 : CAUSAL ? min(ntiles, wq_hi / kKBlock + 1) : ntiles;
+  auto softmax_step = [&](int u) {
+    if (u < nact) {
+      const int k0 = u * kKBlock;
+      const bool full = (k0 + kKBlock <= n) && (!CAUSAL || k0 + kKBlock - 1 <= wq_lo);
+      if (!full) mx_mask<CAUSAL>(c.S, k0, n, qrow, gg);
+      mx_softmax<D>(c, a.c2);
+    }
+  };
+  for (int t = 0; t < ntiles; ++t) {
+    if (lead && t + kAhead < ntiles)
+      issue_mx_tile<D>(kbase, kbytes, vbase, vbytes, abase, abytes, t + kAhead,
+                       smem + ((t + kAhead) % kRingStages) * G::STAGE, w, lane);
+    if (!lead && t > 0) softmax_step(t - 1);
+    if (t <= nact && nact > 0) {
+      const char* cur = smem + (t % kRingStages) * G::STAGE;
+      const char* prev = smem + ((t == 0 ? 0 : t - 1) % kRingStages) * G::STAGE;
+      mx_matrix<D>(cur, prev + G::KBYTES, cur + G::KBYTES + G::VBYTES, prev + G::KBYTES + G::VBYTES, lane, r32,
+                   gg, c);
+    }
+    if (lead) softmax_step(t);
+    if (lead) wait_tiles<L>(max(0, min(kAhead - 1, ntiles - 2 - t)));
+    barrier_only();
+  }
+  if (!lead && ntiles > 0) softmax_step(ntiles - 1);
+  if (nact == ntiles && ntiles > 0) {
+    // PV of the last tile (its QKᵀ part is not needed)
+    const char* prev = smem + ((ntiles - 1) % kRingStages) * G::STAGE;
+    const v4i* lv = reinterpret_cast<const v4i*>(prev + G::KBYTES);
+    const int vsc = *reinterpret_cast<const int*>(prev + G::KBYTES + G::VBYTES + 512 + 4 * lane);
+    c.O[0] = mx_mfma<0, 0>(lv[0 * 64 + lane], c.pk, c.O[0], vsc, c.psc);
+    c.O[1] = mx_mfma<1, 0>(lv[1 * 64 + lane], c.pk, c.O[1], vsc, c.psc);
+    if (D == 128) {
+      c.O[DT - 2] = mx_mfma<2, 0>(lv[(DT - 2) * 64 + lane], c.pk, c.O[DT - 2], vsc, c.psc);
+      c.O[DT - 1] = mx_mfma<3, 0>(lv[(DT - 1) * 64 + lane], c.pk, c.O[DT - 1], vsc, c.psc);
+    }
+  }
+
+  const float l_tot = pair_sum(c.l_run);
+  if (!wave_rows || qrow >= n) return;
+  const float inv = 1.f / l_tot;
+  if (a.lse && gg == 0) a.lse[row0 + qrow] = (c.m_run + __builtin_log2f(l_tot)) * 0.6931471805599453f;
+  uint16_t* __restrict__ orow = a.o + (row0 + qrow) * D;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * dt + 8 * q4 + 4 * gg;
+      v2h lo = {(_Float16)(c.O[dt][4 * q4] * inv), (_Float16)(c.O[dt][4 * q4 + 1] * inv)};
+      v2h hi = {(_Float16)(c.O[dt][4 * q4 + 2] * inv), (_Float16)(c.O[dt][4 * q4 + 3] * inv)};
+      uint2 stv;
+      stv.x = __builtin_bit_cast(uint32_t, lo);
+      stv.y = __builtin_bit_cast(uint32_t, hi);
+      *reinterpret_cast<uint2*>(orow + d) = stv;
+    }
+}
+
+void launch_attn_mx(const MxArgs& a, bool causal, hipStream_t st) {
+  const int64_t blocks = (int64_t)a.g.B * a.g.H * ceil_div(a.g.N, kAttnRows);
+  const dim3 grid((unsigned)blocks), block(kAttnThreads);
+  if (a.g.d == 128) {
+    if (causal) hipLaunchKernelGGL((attn_mx_kernel<128, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_mx_kernel<128, false>), grid, block, 0, st, a);
+  } else {
+    if (causal) hipLaunchKernelGGL((attn_mx_kernel<64, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((attn_mx_kernel<64, false>), grid, block, 0, st, a);
+  }
+}
+
 // Test hook: the int32 Q̂K̂ᵀ tiles computed by the same tile DMA and QKᵀ device
 // code as the attention kernel.
 template <int D>

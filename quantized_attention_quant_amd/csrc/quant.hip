@@ -437,6 +437,146 @@ __global__ __launch_bounds__(kThreads) void v_prepare_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 (dtcms summary, section "SageAttention 3": microscaling FP4 attention,
+// two-level quantisation, range adjusted against block outliers): OCP MX
+// blocks of 32 e2m1 elements sharing one E8M0 (power-of-two) scale, the
+// smallest one under which the block maximum fits e2m1's largest value 6.
+
+// LDS row of key κ of a 64-key tile in the MXFP4 attention kernel: the K̂ rows
+// are stored so that each MFMA lane half's 32 scores are 32 consecutive keys
+// (LDS row 32s + 8q + 4g + t holds key 32g + 16s + 4q + t).
+__device__ __forceinline__ int mx_krow_of_key(int kappa) {
+  return 32 * ((kappa >> 4) & 1) + 8 * ((kappa >> 2) & 3) + 4 * (kappa >> 5) + (kappa & 3);
+}
+
+// Q (SMOOTH = false) or the smoothed K (SMOOTH = true: x = fp32(k) - km, km
+// from the exact column sums, written to kmean by the first workgroup) as MX
+// FP4 along channels: per token, 32-channel blocks.  Codes [row][D/2] bytes,
+// channel c in nibble c%2 of byte c/2.  Scale bytes (X + 127) of block
+// b = 2kk + g: Q into qscale[row][g] dword, byte kk; K into the K/V tile's aux
+// region at (LDS row of the key)·8 + 4g + kk.  D/8 threads per token.
+// Grid (ceil(Nmax/ROWS), H, B).
+template <int D, int ROWS, bool SMOOTH>
+__global__ __launch_bounds__(kThreads) void mx_rows_kernel(const uint16_t* __restrict__ x16, SeqGeom g,
+                                                           const long long* __restrict__ colsum,
+                                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ qscale,
+                                                           uint8_t* __restrict__ aux, float* __restrict__ kmean) {
+  constexpr int CG = D / 8, RPP = kThreads / CG, PASSES = ROWS / RPP;
+  static_assert(PASSES * RPP == ROWS, "rows must be a multiple of rows per pass");
+  const int b = blockIdx.z, h = blockIdx.y;
+  int64_t row0;
+  int n;
+  hs_rows(g, b, h, row0, n);
+  const int t0 = blockIdx.x * ROWS;
+  if (t0 >= n) return;
+  const int cg = threadIdx.x % CG, rr = threadIdx.x / CG;
+  const int64_t hs = (int64_t)b * g.H + h;
+  v4i raw[PASSES];
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + rr + p * RPP;
+    raw[p] = (t < n) ? *reinterpret_cast<const v4i*>(x16 + (row0 + t) * D + cg * 8) : v4i{0, 0, 0, 0};
+  }
+  float shift[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (SMOOTH) {
+    __shared__ float km_s[D];
+    if (threadIdx.x < D) {
+      const float km = (float)((double)colsum[hs * D + threadIdx.x] * 0x1p-24 / (double)n);
+      km_s[threadIdx.x] = km;
+      if (blockIdx.x == 0) kmean[hs * D + threadIdx.x] = km;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) shift[j] = km_s[cg * 8 + j];
+  }
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int t = t0 + rr + p * RPP;
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t w = (uint32_t)raw[p][j];
+      x[2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu)) - shift[2 * j];
+      x[2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)) - shift[2 * j + 1];
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));  // the block's four lanes
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int X = mx_exponent(amax);
+    const uint32_t w = mx_pack8(x, ldexpf(1.f, X));
+    if (t < n) {
+      *reinterpret_cast<uint32_t*>(codes + (row0 + t) * (D / 2) + cg * 4) = w;
+      if ((cg & 3) == 0) {
+        const int blk = cg >> 2, kk = blk >> 1, gsel = blk & 1;
+        const uint8_t sb = (uint8_t)(X + 127);
+        if (!SMOOTH)
+          qscale[(row0 + t) * 8 + 4 * gsel + kk] = sb;
+        else
+          aux[vtile_index(g, b, h, t / kKBlock) * kMxAuxBytes + mx_krow_of_key(t % kKBlock) * 8 + 4 * gsel + kk] =
+              sb;
+      }
+    }
+  }
+}
+
+// V as MX FP4 along keys, one 64-key tile per workgroup: for each channel c
+// and key half g, the block of keys 64t + 32g .. +31 (zeros past n).  Packed
+// in the PV operand order: codes[tile][dt][lane] 16 bytes, lane = c%32 + 32g,
+// dt = c/32, key 32g + j in nibble j; scale byte of (c, g) at aux offset
+// 512 + 4·lane + dt.  Grid (ceil(Nmax/64), H, B).
+template <int D>
+__global__ __launch_bounds__(kThreads) void mx_v_prepare_kernel(const uint16_t* __restrict__ v, SeqGeom g,
+                                                                uint8_t* __restrict__ vcodes,
+                                                                uint8_t* __restrict__ aux) {
+  const int b = blockIdx.z, h = blockIdx.y, kb = blockIdx.x;
+  int64_t row0;
+  int n;
+  hs_rows(g, b, h, row0, n);
+  const int t0 = kb * kKBlock;
+  if (t0 >= n) return;
+  __shared__ uint16_t tile[kKBlock][D + 2];
+  constexpr int CPR = D / 8;
+  for (int idx = threadIdx.x; idx < kKBlock * CPR; idx += kThreads) {
+    const int r = idx / CPR, c = idx % CPR;
+    v4i val = {0, 0, 0, 0};
+    if (t0 + r < n) val = *reinterpret_cast<const v4i*>(v + (row0 + t0 + r) * D + c * 8);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      tile[r][c * 8 + 2 * j] = (uint16_t)((uint32_t)val[j] & 0xffffu);
+      tile[r][c * 8 + 2 * j + 1] = (uint16_t)((uint32_t)val[j] >> 16);
+    }
+  }
+  __syncthreads();
+  const int64_t ti = vtile_index(g, b, h, kb);
+  for (int u = threadIdx.x; u < 2 * D; u += kThreads) {
+    const int c = u % D, gsel = u / D;
+    float x[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      x[j] = (float)__builtin_bit_cast(_Float16, tile[32 * gsel + j][c]);
+      amax = fmaxf(amax, fabsf(x[j]));
+    }
+    const int X = mx_exponent(amax);
+    const float sc = ldexpf(1.f, X);
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float y[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) y[j] = x[8 * q + j];
+      w[q] = mx_pack8(y, sc);
+    }
+    const int lane = (c & 31) + 32 * gsel, dt = c >> 5;
+    *reinterpret_cast<v4i*>(vcodes + (ti * (D / 32) + dt) * 1024 + lane * 16) =
+        v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};
+    aux[ti * kMxAuxBytes + 512 + 4 * lane + dt] = (uint8_t)(X + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side launchers.
 static inline dim3 hs_grid(const SeqGeom& g, int rows) { return dim3(ceil_div(g.N, rows), g.H, g.B); }
 constexpr int kRowsPerBlock = 64;  // rows per workgroup of the per-token quantiser
@@ -480,6 +620,31 @@ void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const 
   else
     SAGE_QUANT(64);
 #undef SAGE_QUANT
+}
+
+void launch_mx_prepare(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, const void* v,
+                       uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes, uint8_t* aux, uint8_t* v_codes,
+                       float* k_mean, long long* colsum, hipStream_t st) {
+  const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
+  const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
+  const uint16_t* v16 = reinterpret_cast<const uint16_t*>(v);
+  launch_zero(colsum, sizeof(long long) * (size_t)gk.B * gk.H * gk.d, st);
+  const dim3 blk(kThreads);
+#define SAGE_MXPREP(DD)                                                                                         \
+  do {                                                                                                         \
+    hipLaunchKernelGGL((k_colsum_kernel<DD>), hs_grid(gk, kColsumChunk), blk, 0, st, k16, gk,                  \
+                       reinterpret_cast<unsigned long long*>(colsum));                                         \
+    hipLaunchKernelGGL((mx_rows_kernel<DD, kRowsPerBlock, false>), hs_grid(gq, kRowsPerBlock), blk, 0, st, q16, \
+                       gq, (const long long*)nullptr, q_codes, q_scales, (uint8_t*)nullptr, (float*)nullptr);  \
+    hipLaunchKernelGGL((mx_rows_kernel<DD, kRowsPerBlock, true>), hs_grid(gk, kRowsPerBlock), blk, 0, st, k16,  \
+                       gk, (const long long*)colsum, k_codes, (uint8_t*)nullptr, aux, k_mean);                 \
+    hipLaunchKernelGGL((mx_v_prepare_kernel<DD>), hs_grid(gk, kKBlock), blk, 0, st, v16, gk, v_codes, aux);     \
+  } while (0)
+  if (gq.d == 128)
+    SAGE_MXPREP(128);
+  else
+    SAGE_MXPREP(64);
+#undef SAGE_MXPREP
 }
 
 void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st) {

@@ -13,6 +13,7 @@ constexpr int kKBlock = 64;   // tokens per K scale block == keys per attention 
 constexpr int kThreads = 256; // 4 wavefronts of 64
 constexpr float kInt8Max = 127.0f;
 constexpr float kE4M3Max = 448.0f;
+constexpr int kMxAuxBytes = 1024;  // MXFP4: per K/V tile, K scales (512 B) + V scales (256 B) + pad
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -72,6 +73,28 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   const int q = total / kXcd, r = total % kXcd;
   const int x = bid % kXcd, local = bid / kXcd;
   return x * q + (x < r ? x : r) + local;
+}
+
+// MXFP4 block exponent (OCP microscaling, E8M0 range): the smallest X with
+// amax <= 6·2^X, 6 being e2m1's largest value.  With amax = f·2^e,
+// f in [0.5, 1): X = e - 3 + (f > 0.75); clamped to [-127, 127]; amax = 0
+// gives -127.
+__device__ __forceinline__ int mx_exponent(float amax) {
+  int e = 0;
+  const float f = frexpf(amax, &e);
+  const int X = e - 3 + (f > 0.75f ? 1 : 0);
+  return amax > 0.f ? max(-127, min(127, X)) : -127;
+}
+
+// Eight values as e2m1 nibbles of fp4(x / scale) (value j at bits 4j; round to
+// nearest even, saturating at ±6 — the hardware conversion).
+__device__ __forceinline__ uint32_t mx_pack8(const float (&x)[8], float scale) {
+  int w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[6], x[7], scale, 3);
+  return (uint32_t)w;
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -26,6 +26,20 @@ struct AttnArgs {
   bool q_per_token = false;  // q_scale holds one scale per query row
 };
 
+// MXFP4 attention (the operands of launch_mx_prepare).
+struct MxArgs {
+  const uint8_t* q;        // e2m1 codes [rows][d/2]
+  const uint8_t* q_scale;  // E8M0 bytes [rows][2 dwords]: dword g, byte kk = block 2kk + g
+  const uint8_t* k;        // e2m1 codes of the smoothed K [Hkv rows][d/2]
+  const uint8_t* v;        // packed V tiles (e2m1 codes)
+  const uint8_t* aux;      // per K/V tile: K scales (by LDS row) and V scales
+  uint16_t* o;
+  float* lse;
+  SeqGeom g;
+  int kv_group;
+  float c2;                // softmax scale times log2(e)
+};
+
 // Inputs and outputs of the Q-smoothing term kernel (smooth_q.hip).
 struct QBiasArgs {
   const uint16_t* k;       // fp16 K, Hkv heads
@@ -48,9 +62,13 @@ void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const 
                      float* q_mean, bool q_per_token, long long* colsum, hipStream_t st);
 void launch_q_bias(const QBiasArgs& a, hipStream_t st);
 void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st);
+void launch_mx_prepare(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, const void* v,
+                       uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes, uint8_t* aux, uint8_t* v_codes,
+                       float* k_mean, long long* colsum, hipStream_t st);
 void launch_v_prepare(const SeqGeom& g, const void* v, const float* v_scale, bool fp8, bool rowmajor,
                       void* out, hipStream_t st);
 void launch_attn(const AttnArgs& a, bool causal, bool fp8, hipStream_t st);
+void launch_attn_mx(const MxArgs& a, bool causal, hipStream_t st);
 void launch_qk_tiles(const int8_t* q, const int8_t* k, int B, int H, int N, int d, const int32_t* list,
                      int n, int32_t* out, hipStream_t st);
 

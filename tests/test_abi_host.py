@@ -74,6 +74,14 @@ def test_workspace_sizes():
     assert to[3] - to[2] == 256 * ((2 * 256 * 4 + 255) // 256)
     assert offs[3] - offs[2] == 256
     assert sage.sage_attn_workspace_size(1, 2, 256, 64, "fp8", smooth_q=True, q_per_token=True) == 0
+    # MXFP4: e2m1 Q and K (half a byte per element), Q scales (8 B per row),
+    # 1 KB of scales per K/V tile, e2m1 V tiles
+    mo = sage.sage_test_workspace_layout(False, 1, 2, 256, 0, 64, "mxfp4")
+    assert mo[1] - mo[0] == 2 * 256 * 32 and mo[2] - mo[1] == 2 * 256 * 32
+    assert mo[3] - mo[2] == 2 * 256 * 8 and mo[4] - mo[3] == 2 * 4 * 1024
+    assert mo[6] - mo[5] == 2 * 4 * 64 * 32
+    assert sage.sage_attn_workspace_size(1, 2, 256, 64, "mxfp4") == mo[11]
+    assert sage.sage_attn_workspace_size(1, 2, 256, 64, "mxfp4", smooth_q=True) == 0
     # grouped K/V heads shrink every K/V region; invalid groupings give 0
     g = sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16", H_kv=1)
     assert 0 < g < sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16")
@@ -105,7 +113,9 @@ def _fwd(**over):
     (dict(B=-1), INVALID),
     (dict(H=0), INVALID),
     (dict(N=(1 << 23) + 1), INVALID),
-    (dict(pv=2), INVALID),
+    (dict(pv=3), INVALID),
+    (dict(pv=2, smooth=1), UNSUPPORTED),     # MXFP4 takes no options
+    (dict(pv=2, smooth=2), UNSUPPORTED),
     (dict(layout=1), UNSUPPORTED),
     (dict(sm=float("nan")), INVALID),
     (dict(sm=float("inf")), INVALID),
