@@ -82,7 +82,7 @@ __all__ = [
     "qk_int", "sage_attention_rows", "sdpa_fp64_rows", "head_views_dense",
     "head_views_varlen", "q_block_mean", "quant_q_smooth", "q_smooth_bias", "quant_q_per_token",
     "E2M1_MAX", "MX_BLOCK", "e2m1_decode", "e2m1_encode", "mx_block_exponent", "mx_quantize",
-    "quant_mxfp4_qk", "quant_mxfp4_v", "mxfp4_decode", "mxfp4_attention_rows",
+    "quant_mxfp4_qk", "quant_mxfp4_v", "mxfp4_decode", "mxfp4_attention_rows", "quant_mxfp4_q_smooth",
 ]
 
 
@@ -444,6 +444,18 @@ def quant_mxfp4_qk(q: np.ndarray, k: np.ndarray):
     km = k_token_mean(k)
     kc, kx = mx_quantize(smooth_k(k, km), -1)
     return qc, qx, kc, kx, km
+
+
+def quant_mxfp4_q_smooth(q: np.ndarray):
+    """Q smoothed by its 128-token block mean (the rule of ``q_block_mean``),
+    then MX FP4 along channels: x = fp32(q) - q̄.  Returns (codes, X, q_mean);
+    the score term the mean carries is ``q_smooth_bias``, added to the scores
+    of the block's rows as for the INT8 path."""
+    n = q.shape[-2]
+    qm = q_block_mean(q)
+    x = q.astype(np.float32) - np.repeat(qm, Q_BLOCK, axis=-2)[..., :n, :]
+    codes, X = mx_quantize(x.astype(np.float32), -1)
+    return codes, X, qm
 
 
 def quant_mxfp4_v(v: np.ndarray):

@@ -829,3 +829,34 @@ def test_mxfp4_close_to_exact_attention_and_envelope():
             assert (diff <= W + slack).all(), (causal, trial, (diff - W - slack).max())
             moved += int((diff > slack).sum())
         assert moved > 0
+
+
+def test_mxfp4_q_smoothing_pins():
+    """The smoothed MXFP4 Q is the MX quantiser on fp32(q) minus the block
+    mean; a constant Q block quantises to all-zero codes, leaving the exact
+    smoothing term as the whole score; on a token-shared Q bias smoothing
+    brings MXFP4 much closer to exact attention."""
+    rng = np.random.default_rng(87)
+    n, d = 300, 64
+    q = (rng.standard_normal((n, d)) + 3 * rng.standard_normal(d)).astype(np.float16)
+    k = (rng.standard_normal((n, d)) + 3 * rng.standard_normal(d)).astype(np.float16)
+    v = rng.standard_normal((n, d)).astype(np.float16)
+    rc, rx, qm = O.quant_mxfp4_q_smooth(q)
+    assert (qm.view(np.uint32) == O.q_block_mean(q).view(np.uint32)).all()
+    want_c, want_x = O.mx_quantize((q.astype(np.float32) - np.repeat(qm, 128, axis=0)[:n]).astype(np.float32), -1)
+    assert (rc == want_c).all() and (rx == want_x).all()
+    sm = float(O.default_sm_scale(d))
+    qc, qx, kc, kx, km = O.quant_mxfp4_qk(q, k)
+    vc, vx = O.quant_mxfp4_v(v)
+    bias = O.q_smooth_bias(qm, k, km, sm)
+    rows = np.arange(n)
+    ref = O.sdpa_fp64_rows(q, k, v, rows, False)
+    plain = cos(O.mxfp4_attention_rows(qc, qx, kc, kx, vc, vx, rows, False, sm), ref)
+    smooth = cos(O.mxfp4_attention_rows(rc, rx, kc, kx, vc, vx, rows, False, sm, score_bias=bias), ref)
+    assert smooth > plain + 0.01 and smooth >= 0.97
+    const = np.repeat(rng.standard_normal((3, d)), 128, axis=0)[:n].astype(np.float16)
+    cc, cx, cm = O.quant_mxfp4_q_smooth(const)
+    assert (O.e2m1_decode(cc) == 0).all()
+    cb = O.q_smooth_bias(cm, k, km, sm)
+    s_exact = (const.astype(np.float64) @ (k.astype(np.float64) - km.astype(np.float64)).T) * sm
+    assert np.abs(cb[rows // 128] - s_exact).max() <= 1e-6 * np.abs(s_exact).max()
