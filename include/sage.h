@@ -72,7 +72,8 @@ typedef enum {
  * the smoothed K, keys for P and V) with one E8M0 power-of-two scale each, the
  * smallest under which the block maximum fits e2m1's largest value 6; P is the
  * online softmax's p = e^(s - m) <= 1 (level one) microscaled per 32-key block
- * (level two).  Takes no options.  Far coarser than the INT8 path (3-bit
+ * (level two).  Takes SAGE_OPT_SMOOTH_Q (not SAGE_OPT_Q_PER_TOKEN: its Q
+ * scales are per row already).  Far coarser than the INT8 path (3-bit
  * elements): about 0.97 cosine to exact attention on Gaussian inputs. */
 typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1, SAGE_MXFP4 = 2 } sage_pv_mode_t;
 
@@ -87,7 +88,9 @@ typedef enum { SAGE_PV_FP16 = 0, SAGE_PV_FP8_E4M3 = 1, SAGE_MXFP4 = 2 } sage_pv_
  *     granularity in "SageAttention 2"); q_scale is then indexed like the Q
  *     rows: [B,H,N] dense, [H,T] varlen.
  * The two are exclusive (SAGE_ERR_UNSUPPORTED): the smoothing term is carried
- * in units of a per-block δQ.  Unknown bits -> SAGE_ERR_INVALID_ARGUMENT. */
+ * in units of a per-block δQ.  With SAGE_MXFP4 the smoothed Q is MX-quantised
+ * and the term, q̄·(k − km) in fp32, starts the score accumulator of every key.
+ * Unknown bits -> SAGE_ERR_INVALID_ARGUMENT. */
 typedef enum { SAGE_OPT_SMOOTH_Q = 1, SAGE_OPT_Q_PER_TOKEN = 2 } sage_option_t;
 typedef enum { SAGE_LAYOUT_HND = 0 } sage_layout_t;
 
@@ -158,7 +161,7 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
  *   for merging partial results over key ranges; 4-byte aligned, no overlap.
  *   is_causal != 0 masks key j > query i (deepseek.csdn.net post: is_causal).
  *   pv_mode selects FP16 PV, FP8-e4m3 PV, or SAGE_MXFP4 (QKᵀ and PV in MXFP4;
- *   options must be 0, else SAGE_ERR_UNSUPPORTED).  options (sage_option_t bits):
+ *   SAGE_OPT_Q_PER_TOKEN -> SAGE_ERR_UNSUPPORTED).  options (sage_option_t bits):
  *   SAGE_OPT_SMOOTH_Q — Q̂ and δQ come from Q minus its block mean and every
  *   score of a row of block b gets sm_scale·q̄_b·(k_j − km) added back
  *   (carried within one unit of δQ·δK; the workspace is then larger);
@@ -219,7 +222,10 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  *   K/V tile 1 KB of scales (K: 8 bytes per key in the kernel's row order;
  *   V: at 512 + 4·lane + dt), [4] k_mean, [5] packed V codes per tile
  *   ([dt][lane] 16 bytes: channel 32dt + lane%32, keys 32(lane/32) + j in
- *   nibble j), [6]-[10] empty.
+ *   nibble j), [6] empty, and with SAGE_OPT_SMOOTH_Q [7] q_mean fp32
+ *   [B,H,nqb,d] and [8] the score term fp32 [B,H,nqb,npad], q̄_b·x_j before
+ *   the softmax scale (keys past a sequence's end: 0; causal: blocks that
+ *   see no key of a tile are not written), else [7]-[8] empty; [9]-[10] empty.
  *   For dense calls pass B,H,H_kv,N,d (total_tokens ignored); for varlen pass
  *   B = nseq, N = max_seqlen and total_tokens.  offsets_out is HOST memory.
  *   The int8/scale/mean regions use the same layouts as sage_quant_qk, with

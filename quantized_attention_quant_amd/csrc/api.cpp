@@ -49,11 +49,14 @@ WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d
   const int64_t vtiles = varlen ? (int64_t)Hkv * sage::vtiles_per_head_varlen(T, B) : (int64_t)B * Hkv * nkb;
   if (pv_mode == SAGE_MXFP4) {
     // [0] Q e2m1 codes [1] K codes [2] Q scales (8 B per row) [3] per-tile
-    // K/V scales [4] k_mean [5] packed V codes [7] K column sums
+    // K/V scales [4] k_mean [5] packed V codes [7] K column sums; with a
+    // smoothed Q [8] q_mean and [9] the fp32 score term per (Q block, key)
+    const size_t qblocks = smooth_q ? (size_t)B * H * nqb : 0;
     const size_t sizes[kWsRegions] = {
         (size_t)(tokens * d / 2), (size_t)(ktokens * d / 2), (size_t)tokens * 8,
         (size_t)vtiles * sage::kMxAuxBytes, sizeof(float) * (size_t)B * Hkv * d,
-        (size_t)vtiles * sage::kKBlock * d / 2, 0, sizeof(long long) * (size_t)B * Hkv * d, 0, 0, 0, 0};
+        (size_t)vtiles * sage::kKBlock * d / 2, 0, sizeof(long long) * (size_t)B * Hkv * d,
+        sizeof(float) * qblocks * d, sizeof(float) * qblocks * (size_t)(nkb * sage::kKBlock), 0, 0};
     WsLayout L;
     size_t cur = 0;
     for (int i = 0; i < kWsRegions; ++i) {
@@ -97,9 +100,10 @@ inline bool options_known(int o) { return (o & ~kKnownOptions) == 0; }
 // Q smoothing carries its term in units of a per-block δQ: not with per-token scales.
 inline bool options_supported(int o) { return (o & kKnownOptions) != kKnownOptions; }
 inline bool pv_mode_ok(sage_pv_mode_t m) { return m == SAGE_PV_FP16 || m == SAGE_PV_FP8_E4M3 || m == SAGE_MXFP4; }
-// MXFP4 has its own Q scales (E8M0 per 32 channels): no Q smoothing or per-token option.
+// MXFP4 has its own Q scales (E8M0 per 32 channels, one row each): Q smoothing
+// only, no per-token option.
 inline bool mode_options_supported(sage_pv_mode_t m, int o) {
-  return options_supported(o) && (m != SAGE_MXFP4 || o == 0);
+  return options_supported(o) && (m != SAGE_MXFP4 || (o & SAGE_OPT_Q_PER_TOKEN) == 0);
 }
 
 sage_status_t check_dims(int B, int H, int N, int d) {
@@ -174,13 +178,24 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   if (pv_mode == SAGE_MXFP4) {
     uint8_t* aux = reinterpret_cast<uint8_t*>(ws + L.off[3]);
     sage::launch_zero(aux, L.off[4] - L.off[3], st);  // K scales of rows past a sequence's end stay 0
+    float* km = reinterpret_cast<float*>(ws + L.off[4]);
+    float* qm = sq ? reinterpret_cast<float*>(ws + L.off[8]) : nullptr;
+    float* terms = reinterpret_cast<float*>(ws + L.off[9]);
     sage::launch_mx_prepare(g, gk, q, k, v, reinterpret_cast<uint8_t*>(ws + L.off[0]),
                             reinterpret_cast<uint8_t*>(ws + L.off[2]), reinterpret_cast<uint8_t*>(ws + L.off[1]), aux,
-                            reinterpret_cast<uint8_t*>(ws + L.off[5]), reinterpret_cast<float*>(ws + L.off[4]),
+                            reinterpret_cast<uint8_t*>(ws + L.off[5]), km, qm,
                             reinterpret_cast<long long*>(ws + L.off[7]), st);
-    const sage::MxArgs a{reinterpret_cast<const uint8_t*>(ws + L.off[0]), reinterpret_cast<const uint8_t*>(ws + L.off[2]),
-                         reinterpret_cast<const uint8_t*>(ws + L.off[1]), reinterpret_cast<const uint8_t*>(ws + L.off[5]),
-                         aux, static_cast<uint16_t*>(o), lse, g, g.H / Hkv, (float)((double)sm * 1.4426950408889634)};
+    if (sq) {
+      // q̄·x in raw score units: the kernel applies the softmax scale to the sum
+      sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, nullptr, qm, nullptr,
+                         reinterpret_cast<int32_t*>(terms), nullptr, nullptr, g, g.H / Hkv, 1.0f, is_causal != 0};
+      qa.raw = 1;
+      sage::launch_q_bias(qa, st);
+    }
+    sage::MxArgs a{reinterpret_cast<const uint8_t*>(ws + L.off[0]), reinterpret_cast<const uint8_t*>(ws + L.off[2]),
+                   reinterpret_cast<const uint8_t*>(ws + L.off[1]), reinterpret_cast<const uint8_t*>(ws + L.off[5]),
+                   aux, static_cast<uint16_t*>(o), lse, g, g.H / Hkv, (float)((double)sm * 1.4426950408889634)};
+    if (sq) a.qb_slots = terms;
     sage::launch_attn_mx(a, is_causal != 0, st);
     return finish(st);
   }
@@ -378,10 +393,11 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
   if (pv_mode == SAGE_MXFP4) {
     float sm;
     resolve_sm_scale(0.f, d, &sm);
-    const sage::MxArgs a{reinterpret_cast<const uint8_t*>(ws + L.off[0]), reinterpret_cast<const uint8_t*>(ws + L.off[2]),
-                         reinterpret_cast<const uint8_t*>(ws + L.off[1]), reinterpret_cast<const uint8_t*>(ws + L.off[5]),
-                         reinterpret_cast<const uint8_t*>(ws + L.off[3]), static_cast<uint16_t*>(o), nullptr, g,
-                         H / H_kv, (float)((double)sm * 1.4426950408889634)};
+    sage::MxArgs a{reinterpret_cast<const uint8_t*>(ws + L.off[0]), reinterpret_cast<const uint8_t*>(ws + L.off[2]),
+                   reinterpret_cast<const uint8_t*>(ws + L.off[1]), reinterpret_cast<const uint8_t*>(ws + L.off[5]),
+                   reinterpret_cast<const uint8_t*>(ws + L.off[3]), static_cast<uint16_t*>(o), nullptr, g,
+                   H / H_kv, (float)((double)sm * 1.4426950408889634)};
+    if (options & SAGE_OPT_SMOOTH_Q) a.qb_slots = reinterpret_cast<const float*>(ws + L.off[9]);
     sage::launch_attn_mx(a, is_causal != 0, reinterpret_cast<hipStream_t>(stream));
     return finish(reinterpret_cast<hipStream_t>(stream));
   }

@@ -701,11 +701,12 @@ void attn_fwd_kernel(AttnArgs a) {
 //   * LDS stage: K̂ codes (rows of d/2 bytes, 16-byte chunks XOR-swizzled on
 //     the 256-byte bank line), packed V codes, and 1 KB of scales (K: 8 bytes
 //     per row; V: 4 bytes per lane).
-template <int D>
+template <int D, bool SM = false>
 struct MxGeom {
   static constexpr int KBYTES = kKBlock * D / 2;  // K̂ codes of a tile
   static constexpr int VBYTES = kKBlock * D / 2;  // packed V codes
-  static constexpr int STAGE = KBYTES + VBYTES + kMxAuxBytes;
+  static constexpr int SBYTES = SM ? 1024 : 0;    // smoothed Q: the term per key, two Q blocks
+  static constexpr int STAGE = KBYTES + VBYTES + kMxAuxBytes + SBYTES;
   static constexpr int KCH = KBYTES / 16;
   static constexpr int CI = (KBYTES + VBYTES) / 16 / kThreads;  // 16-byte DMA instructions per group-A wave
   static constexpr int CPR = D / 32;                             // 16-byte chunks per K̂ row
@@ -720,11 +721,12 @@ __device__ __forceinline__ int mx_key_of_row(int r) {
   return 32 * ((r >> 2) & 1) + 16 * (r >> 5) + 4 * ((r >> 3) & 3) + (r & 3);
 }
 
-template <int D>
+template <int D, bool SM = false>
 __device__ __forceinline__ void issue_mx_tile(const void* kbase, int kbytes, const void* vbase, int vbytes,
-                                              const void* abase, int abytes, int t, char* stage, int w, int lane) {
+                                              const void* abase, int abytes, int t, char* stage, int w, int lane,
+                                              const SlotSrc& ss = SlotSrc{}) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  using G = MxGeom<D>;
+  using G = MxGeom<D, SM>;
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(kbase), (short)0, kbytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rv =
@@ -750,6 +752,15 @@ __device__ __forceinline__ void issue_mx_tile(const void* kbase, int kbytes, con
   // scales: wave w (< 4) brings bytes 256w .. 256w+255 of the tile's 1 KB
   __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + G::KBYTES + G::VBYTES + w * 256), 4,
                                            t * kMxAuxBytes + w * 256 + lane * 4, 0, 0, 0);
+  if (SM) {
+    // the term per key, as for the INT8 path: quarter w holds block w/2, keys
+    // 64t + 32(w%2) + lane (lanes 32-63 read zeros past the range)
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(ss.base), (short)0,
+                                                                        ss.bytes, kBufferFlags);
+    const int off = lane < 32 ? ((w >> 1) * ss.npad + t * kKBlock + 32 * (w & 1) + lane) * 4 : ss.bytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (lds_ptr_t)(stage + G::KBYTES + G::VBYTES + kMxAuxBytes + w * 256), 4, off, 0, 0, 0);
+  }
 #endif
 }
 
@@ -774,10 +785,13 @@ struct MxWave {
 };
 
 // Matrix phase: PV of the previous tile (its P in pk) and QKᵀ of this one.
-template <int D>
+// With a smoothed Q (lslots: the wave's Q block's 64 terms in LDS, quarter
+// layout) the QKᵀ accumulator starts from the term of each key.
+template <int D, bool SM = false>
 __device__ __forceinline__ void mx_matrix(const char* __restrict__ kstage, const char* __restrict__ vstage,
                                           const char* __restrict__ astage, const char* __restrict__ avstage,
-                                          int lane, int r32, int gg, MxWave<D>& c) {
+                                          int lane, int r32, int gg, MxWave<D>& c,
+                                          const float4* __restrict__ lslots = nullptr) {
   using G = MxGeom<D>;
   constexpr int DT = D / 32;
   const v4i* lk = reinterpret_cast<const v4i*>(kstage);
@@ -795,11 +809,29 @@ __device__ __forceinline__ void mx_matrix(const char* __restrict__ kstage, const
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) vf[dt] = lv[dt * 64 + lane];
   const int vsc = *reinterpret_cast<const int*>(avstage + 512 + 4 * lane);
+  float4 init[2][4];
+  if (SM) {
+    // S[s] reg i is key 32gg + 16s + i: four runs of four consecutive keys
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) init[s][q] = lslots[16 * gg + 4 * s + q];
+  }
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     v16f acc;
+    if (SM) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+      for (int q = 0; q < 4; ++q) {
+        acc[4 * q] = init[s][q].x;
+        acc[4 * q + 1] = init[s][q].y;
+        acc[4 * q + 2] = init[s][q].z;
+        acc[4 * q + 3] = init[s][q].w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+    }
     acc = mx_mfma<0, 0>(kf[s][0], c.qf[0], acc, ks[s], c.qsc);
     if (D == 128) acc = mx_mfma<1, 1>(kf[s][D / 64 - 1], c.qf[D / 64 - 1], acc, ks[s], c.qsc);
     c.S[s] = acc;
@@ -812,7 +844,7 @@ __device__ __forceinline__ void mx_matrix(const char* __restrict__ kstage, const
   }
   // schedule: every LDS read first, then the MFMAs (each read has the earlier
   // MFMAs to land behind)
-  __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 64) + 2 + DT + 1, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 2 * (D / 64) + 2 + DT + 1 + (SM ? 8 : 0), 0);
   __builtin_amdgcn_sched_group_barrier(0x008, 2 * (D / 64) + DT, 0);
 }
 
@@ -880,12 +912,12 @@ __device__ __forceinline__ void mx_softmax(MxWave<D>& c, float c2) {
   c.l_run += lsum;
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SM>
 __global__ __attribute__((amdgpu_flat_work_group_size(kAttnThreads, kAttnThreads),
-                          amdgpu_waves_per_eu(kAttnWavesPerSimd<D, false>, kAttnWavesPerSimd<D, false>)))
+                          amdgpu_waves_per_eu(kAttnWavesPerSimd<D, SM>, kAttnWavesPerSimd<D, SM>)))
 void attn_mx_kernel(MxArgs a) {
   constexpr int DT = D / 32;
-  using G = MxGeom<D>;
+  using G = MxGeom<D, SM>;
   __shared__ __attribute__((aligned(1024))) char smem[kRingStages * G::STAGE];
 
   const SeqGeom& g = a.g;
@@ -925,7 +957,13 @@ void attn_mx_kernel(MxArgs a) {
   const int vbytes = ntiles_seq * G::VBYTES;
   const uint8_t* abase = a.aux + tile0 * kMxAuxBytes;
   const int abytes = ntiles_seq * kMxAuxBytes;
-  constexpr int L = G::CI + 1;
+  constexpr int L = G::CI + 1 + (SM ? 1 : 0);
+  const int nqb = ceil_div(g.N, kQBlock), npad = ceil_div(g.N, kKBlock) * kKBlock;
+  const int64_t hs = (int64_t)b * g.H + h;
+  SlotSrc ss{};
+  if (SM)
+    ss = SlotSrc{reinterpret_cast<const int32_t*>(a.qb_slots) + (hs * nqb + q0 / kQBlock) * (int64_t)npad,
+                 (q0 + kQBlock < n ? 2 : 1) * npad * 4, npad};
 
   MxWave<D> c;
 #pragma unroll
@@ -945,7 +983,7 @@ void attn_mx_kernel(MxArgs a) {
   if (lead) {
     const int first = min(kAhead, ntiles);
     for (int t = 0; t < first; ++t)
-      issue_mx_tile<D>(kbase, kbytes, vbase, vbytes, abase, abytes, t, smem + t * G::STAGE, w, lane);
+      issue_mx_tile<D, SM>(kbase, kbytes, vbase, vbytes, abase, abytes, t, smem + t * G::STAGE, w, lane, ss);
   }
   wait_dma<0>();
   barrier_only();
@@ -961,14 +999,16 @@ void attn_mx_kernel(MxArgs a) {
   };
   for (int t = 0; t < ntiles; ++t) {
     if (lead && t + kAhead < ntiles)
-      issue_mx_tile<D>(kbase, kbytes, vbase, vbytes, abase, abytes, t + kAhead,
-                       smem + ((t + kAhead) % kRingStages) * G::STAGE, w, lane);
+      issue_mx_tile<D, SM>(kbase, kbytes, vbase, vbytes, abase, abytes, t + kAhead,
+                           smem + ((t + kAhead) % kRingStages) * G::STAGE, w, lane, ss);
     if (!lead && t > 0) softmax_step(t - 1);
     if (t <= nact && nact > 0) {
       const char* cur = smem + (t % kRingStages) * G::STAGE;
       const char* prev = smem + ((t == 0 ? 0 : t - 1) % kRingStages) * G::STAGE;
-      mx_matrix<D>(cur, prev + G::KBYTES, cur + G::KBYTES + G::VBYTES, prev + G::KBYTES + G::VBYTES, lane, r32,
-                   gg, c);
+      mx_matrix<D, SM>(cur, prev + G::KBYTES, cur + G::KBYTES + G::VBYTES, prev + G::KBYTES + G::VBYTES, lane,
+                       r32, gg, c,
+                       reinterpret_cast<const float4*>(cur + G::KBYTES + G::VBYTES + kMxAuxBytes) +
+                           32 * (wq_lo / kQBlock - q0 / kQBlock));
     }
     if (lead) softmax_step(t);
     if (lead) wait_tiles<L>(max(0, min(kAhead - 1, ntiles - 2 - t)));
@@ -1010,13 +1050,20 @@ void attn_mx_kernel(MxArgs a) {
 void launch_attn_mx(const MxArgs& a, bool causal, hipStream_t st) {
   const int64_t blocks = (int64_t)a.g.B * a.g.H * ceil_div(a.g.N, kAttnRows);
   const dim3 grid((unsigned)blocks), block(kAttnThreads);
+  const bool sm = a.qb_slots != nullptr;
+#define SAGE_MX(DD, CS)                                                                   \
+  do {                                                                                    \
+    if (sm)                                                                               \
+      hipLaunchKernelGGL((attn_mx_kernel<DD, CS, true>), grid, block, 0, st, a);          \
+    else                                                                                  \
+      hipLaunchKernelGGL((attn_mx_kernel<DD, CS, false>), grid, block, 0, st, a);         \
+  } while (0)
   if (a.g.d == 128) {
-    if (causal) hipLaunchKernelGGL((attn_mx_kernel<128, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_mx_kernel<128, false>), grid, block, 0, st, a);
+    if (causal) SAGE_MX(128, true); else SAGE_MX(128, false);
   } else {
-    if (causal) hipLaunchKernelGGL((attn_mx_kernel<64, true>), grid, block, 0, st, a);
-    else hipLaunchKernelGGL((attn_mx_kernel<64, false>), grid, block, 0, st, a);
+    if (causal) SAGE_MX(64, true); else SAGE_MX(64, false);
   }
+#undef SAGE_MX
 }
 
 // Test hook: the int32 Q̂K̂ᵀ tiles computed by the same tile DMA and QKᵀ device

@@ -449,18 +449,24 @@ __device__ __forceinline__ int mx_krow_of_key(int kappa) {
   return 32 * ((kappa >> 4) & 1) + 8 * ((kappa >> 2) & 3) + 4 * (kappa >> 5) + (kappa & 3);
 }
 
-// Q (SMOOTH = false) or the smoothed K (SMOOTH = true: x = fp32(k) - km, km
-// from the exact column sums, written to kmean by the first workgroup) as MX
-// FP4 along channels: per token, 32-channel blocks.  Codes [row][D/2] bytes,
-// channel c in nibble c%2 of byte c/2.  Scale bytes (X + 127) of block
-// b = 2kk + g: Q into qscale[row][g] dword, byte kk; K into the K/V tile's aux
-// region at (LDS row of the key)·8 + 4g + kk.  D/8 threads per token.
-// Grid (ceil(Nmax/ROWS), H, B).
-template <int D, int ROWS, bool SMOOTH>
+// Q, the smoothed K or the smoothed Q as MX FP4 along channels (per token,
+// 32-channel blocks).  MODE (the shifts of quant_block_kernel):
+//   kShiftNone  — Q;
+//   kShiftKMean — K: x = fp32(k) - km, km from the exact column sums, written
+//                 to mean[hs][D] by the first workgroup;
+//   kShiftBlock — smoothed Q: x = fp32(q) - q̄ of the workgroup's own 128-token
+//                 block (ROWS = 128), the exact block mean written to
+//                 mean[hs][blk][D].
+// Codes [row][D/2] bytes, channel c in nibble c%2 of byte c/2.  Scale bytes
+// (X + 127) of block b = 2kk + g: Q into qscale[row][g] dword, byte kk; K
+// into the K/V tile's aux region at (LDS row of the key)·8 + 4g + kk.  D/8
+// threads per token.  Grid (ceil(Nmax/ROWS), H, B).
+template <int D, int ROWS, int MODE>
 __global__ __launch_bounds__(kThreads) void mx_rows_kernel(const uint16_t* __restrict__ x16, SeqGeom g,
                                                            const long long* __restrict__ colsum,
                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ qscale,
-                                                           uint8_t* __restrict__ aux, float* __restrict__ kmean) {
+                                                           uint8_t* __restrict__ aux, float* __restrict__ mean) {
+  constexpr bool SMOOTH = MODE == kShiftKMean;
   constexpr int CG = D / 8, RPP = kThreads / CG, PASSES = ROWS / RPP;
   static_assert(PASSES * RPP == ROWS, "rows must be a multiple of rows per pass");
   const int b = blockIdx.z, h = blockIdx.y;
@@ -483,11 +489,39 @@ __global__ __launch_bounds__(kThreads) void mx_rows_kernel(const uint16_t* __res
     if (threadIdx.x < D) {
       const float km = (float)((double)colsum[hs * D + threadIdx.x] * 0x1p-24 / (double)n);
       km_s[threadIdx.x] = km;
-      if (blockIdx.x == 0) kmean[hs * D + threadIdx.x] = km;
+      if (blockIdx.x == 0) mean[hs * D + threadIdx.x] = km;
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < 8; ++j) shift[j] = km_s[cg * 8 + j];
+  } else if (MODE == kShiftBlock) {
+    static_assert(MODE != kShiftBlock || ROWS == kQBlock, "the block mean needs the whole Q block");
+    // exact: fp64 sums of fp16 values (rows past n loaded as zeros), one
+    // divide by the block's token count, one rounding to fp32
+    double acc[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = (uint32_t)raw[p][j];
+        acc[2 * j] += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+        acc[2 * j + 1] += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+      }
+    __shared__ double part[RPP][D];
+    __shared__ float qm_s[D];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[rr][cg * 8 + j] = acc[j];
+    __syncthreads();
+    if (threadIdx.x < D) {
+      double sum = 0.;
+      for (int r = 0; r < RPP; ++r) sum += part[r][threadIdx.x];
+      const float qm = (float)(sum / (double)min(ROWS, n - t0));
+      qm_s[threadIdx.x] = qm;
+      mean[(hs * ceil_div(g.N, ROWS) + blockIdx.x) * D + threadIdx.x] = qm;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 8; ++j) shift[j] = qm_s[cg * 8 + j];
   }
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
@@ -624,7 +658,7 @@ void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const 
 
 void launch_mx_prepare(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, const void* v,
                        uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes, uint8_t* aux, uint8_t* v_codes,
-                       float* k_mean, long long* colsum, hipStream_t st) {
+                       float* k_mean, float* q_mean, long long* colsum, hipStream_t st) {
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
   const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
   const uint16_t* v16 = reinterpret_cast<const uint16_t*>(v);
@@ -634,10 +668,15 @@ void launch_mx_prepare(const SeqGeom& gq, const SeqGeom& gk, const void* q, cons
   do {                                                                                                         \
     hipLaunchKernelGGL((k_colsum_kernel<DD>), hs_grid(gk, kColsumChunk), blk, 0, st, k16, gk,                  \
                        reinterpret_cast<unsigned long long*>(colsum));                                         \
-    hipLaunchKernelGGL((mx_rows_kernel<DD, kRowsPerBlock, false>), hs_grid(gq, kRowsPerBlock), blk, 0, st, q16, \
-                       gq, (const long long*)nullptr, q_codes, q_scales, (uint8_t*)nullptr, (float*)nullptr);  \
-    hipLaunchKernelGGL((mx_rows_kernel<DD, kRowsPerBlock, true>), hs_grid(gk, kRowsPerBlock), blk, 0, st, k16,  \
-                       gk, (const long long*)colsum, k_codes, (uint8_t*)nullptr, aux, k_mean);                 \
+    if (q_mean)                                                                                                \
+      hipLaunchKernelGGL((mx_rows_kernel<DD, kQBlock, kShiftBlock>), hs_grid(gq, kQBlock), blk, 0, st, q16,     \
+                         gq, (const long long*)nullptr, q_codes, q_scales, (uint8_t*)nullptr, q_mean);         \
+    else                                                                                                       \
+      hipLaunchKernelGGL((mx_rows_kernel<DD, kRowsPerBlock, kShiftNone>), hs_grid(gq, kRowsPerBlock), blk, 0,  \
+                         st, q16, gq, (const long long*)nullptr, q_codes, q_scales, (uint8_t*)nullptr,         \
+                         (float*)nullptr);                                                                     \
+    hipLaunchKernelGGL((mx_rows_kernel<DD, kRowsPerBlock, kShiftKMean>), hs_grid(gk, kRowsPerBlock), blk, 0,   \
+                       st, k16, gk, (const long long*)colsum, k_codes, (uint8_t*)nullptr, aux, k_mean);        \
     hipLaunchKernelGGL((mx_v_prepare_kernel<DD>), hs_grid(gk, kKBlock), blk, 0, st, v16, gk, v_codes, aux);     \
   } while (0)
   if (gq.d == 128)

@@ -38,6 +38,7 @@ struct MxArgs {
   SeqGeom g;
   int kv_group;
   float c2;                // softmax scale times log2(e)
+  const float* qb_slots = nullptr;  // smoothed Q: the term q̄·x per (Q block, key), [B][H][nqb][npad]
 };
 
 // Inputs and outputs of the Q-smoothing term kernel (smooth_q.hip).
@@ -54,6 +55,7 @@ struct QBiasArgs {
   int kv_group;
   float sm_log2e;          // softmax scale times log2(e)
   int causal;              // skip (block, tile) pairs no query of the block sees
+  int raw = 0;             // MXFP4: write q̄·x (fp32, raw score units) for every key; no flags
 };
 
 void launch_zero(void* p, size_t bytes, hipStream_t st);
@@ -64,7 +66,7 @@ void launch_q_bias(const QBiasArgs& a, hipStream_t st);
 void launch_v_scale(const SeqGeom& g, const void* v, float* v_scale, hipStream_t st);
 void launch_mx_prepare(const SeqGeom& gq, const SeqGeom& gk, const void* q, const void* k, const void* v,
                        uint8_t* q_codes, uint8_t* q_scales, uint8_t* k_codes, uint8_t* aux, uint8_t* v_codes,
-                       float* k_mean, long long* colsum, hipStream_t st);
+                       float* k_mean, float* q_mean, long long* colsum, hipStream_t st);
 void launch_v_prepare(const SeqGeom& g, const void* v, const float* v_scale, bool fp8, bool rowmajor,
                       void* out, hipStream_t st);
 void launch_attn(const AttnArgs& a, bool causal, bool fp8, hipStream_t st);

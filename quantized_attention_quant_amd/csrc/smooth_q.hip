@@ -23,6 +23,10 @@
 //   flags[hs][b][2t + s] = 1 (half s of tile t), with fix[hs][b][j] = Δ·log2e
 //     (fp32) for its keys: the attention kernel then adds Δ in fp32.
 //
+// MXFP4 (raw): the scores accumulate in fp32, so the term needs no integer
+// form: slots[hs][b][j] holds q̄_b · x_j itself (fp32 bits, raw score units,
+// before the softmax scale) for every key, and no flags are written.
+//
 // The contraction q̄_b · x_j runs on the fp16 MFMA.  Both operands are scaled
 // by powers of two into [-1, 1] (q̄_b by 2^-eq_b from its largest channel, x_j
 // by 2^-ek_t from its K block's scale) and split into fp16 hi + lo parts;
@@ -100,37 +104,51 @@ __global__ __launch_bounds__(kThreads) void q_bias_kernel(QBiasArgs a) {
   __syncthreads();
 
   // A operand: x_j / 2^ek as fp16 hi/lo; lane holds key kw0 + r32, channels
-  // 16·kk + 8·gg .. +7 (zeros past n)
-  const float dk = wave_live ? a.k_scale[hsk * nkb + t] : 0.f;
-  const int ek = pow2_above(128.f * dk);  // 128·δK > max|x| of the K block
-  const float kscale = ldexpf(1.f, -ek);
-  v8h ahi[KS], alo[KS];
+  // 16·kk + 8·gg .. +7 (zeros past n).  2^ek > max|x|: from the K block's
+  // INT8 scale (128·δK), or in raw mode from this wave's own keys.
+  const int key = kw0 + r32;
+  float xs[KS][8];
   {
-    const int key = kw0 + r32;
     v4i raw[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk)
       raw[kk] = (key < n) ? *reinterpret_cast<const v4i*>(a.k + (krow0 + key) * D + 16 * kk + 8 * gg)
                           : v4i{0, 0, 0, 0};
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      float x[8];
+    for (int kk = 0; kk < KS; ++kk)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t wd = (uint32_t)raw[kk][j];
         const int c = 16 * kk + 8 * gg + 2 * j;
-        // the smoothed K exactly as the K quantiser forms it, then scaled
-        x[2 * j] = (key < n) ? ((float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xffffu)) - km_s[c]) * kscale
-                             : 0.f;
-        x[2 * j + 1] =
-            (key < n) ? ((float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16)) - km_s[c + 1]) * kscale : 0.f;
+        // the smoothed K exactly as the K quantiser forms it
+        xs[kk][2 * j] = (key < n) ? (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xffffu)) - km_s[c] : 0.f;
+        xs[kk][2 * j + 1] = (key < n) ? (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16)) - km_s[c + 1] : 0.f;
       }
-      ahi[kk] = split_hi(x);
-      alo[kk] = split_lo(x, ahi[kk]);
-    }
+  }
+  float dk = 0.f;
+  int ek;
+  if (a.raw) {
+    float mx = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, fabsf(xs[kk][j]));
+    ek = pow2_above(wave_max(mx));
+  } else {
+    dk = wave_live ? a.k_scale[hsk * nkb + t] : 0.f;
+    ek = pow2_above(128.f * dk);  // 128·δK > max|x| of the K block
+  }
+  const float kscale = ldexpf(1.f, -ek);
+  v8h ahi[KS], alo[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = xs[kk][j] * kscale;
+    ahi[kk] = split_hi(x);
+    alo[kk] = split_lo(x, ahi[kk]);
   }
 
-  const float* __restrict__ dq_row = a.q_scale + hs * nqb;
   const int ngroups = ceil_div(nqb_seq, kQbBlocksPerGroup);
   for (int grp = 0; grp < ngroups; ++grp) {
     // --- B operand of 32 Q blocks: q̄_b / 2^eq_b as fp16 hi/lo in LDS
@@ -184,37 +202,54 @@ __global__ __launch_bounds__(kThreads) void q_bias_kernel(QBiasArgs a) {
       const int bb = grp * kQbBlocksPerGroup + r32;
       const bool blk_live = bb < nqb_seq && !(a.causal && kKBlock * t > kQBlock * bb + kQBlock - 1);
       const float f = ldexpf(a.sm_log2e, eq_s[r32] + ek);
-      const float dq = bb < nqb_seq ? dq_row[bb] : 0.f;
-      const float c2 = dq * dk * kLog2eF;  // the attention kernel's per-tile factor
-      const float inv = 1.f / c2;
-      float dl[16];
-      bool fits = c2 >= 1.17549435e-38f && c2 <= 3.0e38f;
+      if (a.raw) {
+        // q̄·x in raw score units (sm_log2e = 1 here), every key, no flags
+        if (blk_live) {
+          const int64_t rowoff = (hs * nqb + bb) * (int64_t)npad;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dl[i] = acc[i] * f;
-        const int key = kw0 + 8 * (i >> 2) + 4 * gg + (i & 3);
-        fits = fits && (key >= n || __builtin_fabsf(dl[i] * inv) <= (float)kSlotLimit<D>);
-      }
-      // both lanes of the block (gg = 0, 1) hold half of the 32 keys
-      const int other = __shfl_xor((int)fits, 32);
-      fits = fits && other;
-      if (blk_live) {
-        const int64_t rowoff = (hs * nqb + bb) * (int64_t)npad;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int key0 = kw0 + 8 * q4 + 4 * gg;
-          int sv[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = 4 * q4 + j;
-            sv[j] = (fits && key0 + j < n) ? kMagicBias + (int)__builtin_rintf(dl[i] * inv) : kMagicBias;
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int key0 = kw0 + 8 * q4 + 4 * gg;
+            float4 vv;
+            vv.x = acc[4 * q4] * f;
+            vv.y = acc[4 * q4 + 1] * f;
+            vv.z = acc[4 * q4 + 2] * f;
+            vv.w = acc[4 * q4 + 3] * f;
+            *reinterpret_cast<float4*>(a.slots + rowoff + key0) = vv;
           }
-          *reinterpret_cast<v4i*>(a.slots + rowoff + key0) = v4i{sv[0], sv[1], sv[2], sv[3]};
-          if (!fits)
-            *reinterpret_cast<float4*>(a.fix + rowoff + key0) =
-                float4{dl[4 * q4], dl[4 * q4 + 1], dl[4 * q4 + 2], dl[4 * q4 + 3]};
         }
-        if (gg == 0) a.flags[(hs * nqb + bb) * (int64_t)(2 * nkb) + 2 * t + s] = fits ? 0 : 1;
+      } else {
+        const float dq = bb < nqb_seq ? a.q_scale[hs * nqb + bb] : 0.f;
+        const float c2 = dq * dk * kLog2eF;  // the attention kernel's per-tile factor
+        const float inv = 1.f / c2;
+        float dl[16];
+        bool fits = c2 >= 1.17549435e-38f && c2 <= 3.0e38f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          dl[i] = acc[i] * f;
+          const int key = kw0 + 8 * (i >> 2) + 4 * gg + (i & 3);
+          fits = fits && (key >= n || __builtin_fabsf(dl[i] * inv) <= (float)kSlotLimit<D>);
+        }
+        // both lanes of the block (gg = 0, 1) hold half of the 32 keys
+        const int other = __shfl_xor((int)fits, 32);
+        fits = fits && other;
+        if (blk_live) {
+          const int64_t rowoff = (hs * nqb + bb) * (int64_t)npad;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int key0 = kw0 + 8 * q4 + 4 * gg;
+            int sv[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int i = 4 * q4 + j;
+              sv[j] = (fits && key0 + j < n) ? kMagicBias + (int)__builtin_rintf(dl[i] * inv) : kMagicBias;
+            }
+            *reinterpret_cast<v4i*>(a.slots + rowoff + key0) = v4i{sv[0], sv[1], sv[2], sv[3]};
+            if (!fits)
+              *reinterpret_cast<float4*>(a.fix + rowoff + key0) =
+                  float4{dl[4 * q4], dl[4 * q4 + 1], dl[4 * q4 + 2], dl[4 * q4 + 3]};
+          }
+          if (gg == 0) a.flags[(hs * nqb + bb) * (int64_t)(2 * nkb) + 2 * t + s] = fits ? 0 : 1;
+        }
       }
     }
     __syncthreads();  // the next group overwrites the B operand

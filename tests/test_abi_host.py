@@ -81,7 +81,12 @@ def test_workspace_sizes():
     assert mo[3] - mo[2] == 2 * 256 * 8 and mo[4] - mo[3] == 2 * 4 * 1024
     assert mo[6] - mo[5] == 2 * 4 * 64 * 32
     assert sage.sage_attn_workspace_size(1, 2, 256, 64, "mxfp4") == mo[11]
-    assert sage.sage_attn_workspace_size(1, 2, 256, 64, "mxfp4", smooth_q=True) == 0
+    # with Q smoothing: q_mean [B,H,nqb,d] and the fp32 term [B,H,nqb,npad]
+    ms = sage.sage_test_workspace_layout(False, 1, 2, 256, 0, 64, "mxfp4", smooth_q=True)
+    assert ms[:7] == mo[:7]
+    assert ms[8] - ms[7] == 2 * 2 * 64 * 4 and ms[9] - ms[8] == 2 * 2 * 256 * 4
+    assert ms[9] == ms[10] == ms[11] == sage.sage_attn_workspace_size(1, 2, 256, 64, "mxfp4", smooth_q=True)
+    assert sage.sage_attn_workspace_size(1, 2, 256, 64, "mxfp4", q_per_token=True) == 0
     # grouped K/V heads shrink every K/V region; invalid groupings give 0
     g = sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16", H_kv=1)
     assert 0 < g < sage.sage_attn_workspace_size(1, 4, 256, 64, "fp16")
@@ -114,8 +119,9 @@ def _fwd(**over):
     (dict(H=0), INVALID),
     (dict(N=(1 << 23) + 1), INVALID),
     (dict(pv=3), INVALID),
-    (dict(pv=2, smooth=1), UNSUPPORTED),     # MXFP4 takes no options
-    (dict(pv=2, smooth=2), UNSUPPORTED),
+    (dict(pv=2, smooth=2), UNSUPPORTED),     # MXFP4: no per-token option (its Q scales are per row)
+    (dict(pv=2, smooth=3), UNSUPPORTED),
+    (dict(pv=2, smooth=1, wsb=sage.sage_attn_workspace_size(1, 2, 256, 64, "mxfp4")), WS_SMALL),
     (dict(layout=1), UNSUPPORTED),
     (dict(sm=float("nan")), INVALID),
     (dict(sm=float("inf")), INVALID),
