@@ -346,7 +346,8 @@ def _sample_rows(n, rng, k=48):
     return np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, n - 1], rng.choice(n, size=min(n, k), replace=False)]))
 
 
-@pytest.mark.parametrize("name", ["tiny", "llm_prefill", "video_dit", "video_dit_biasx20", "long_fp8", "seq16k"])
+@pytest.mark.parametrize("name", ["tiny", "llm_prefill", "video_dit", "video_dit_biasx20", "long_fp8", "seq16k",
+                                  "seq16k_causal"])
 def test_dense_workload(name):
     w = workloads.get(name)
     say(f"case workload {name} {w.description}")

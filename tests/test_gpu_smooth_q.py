@@ -97,6 +97,27 @@ def o1_rows(quant, k_head, v_head, b, h, rows, causal, pv_mode, vq=None):
     return o, bias, (qi, qs, ki, ks), bound
 
 
+def fit_decisions(quant, k_head, b, h, n, d):
+    """Per (Q block, tile, half): the halves whose integer terms surely fit
+    (every |Δ·log2e / c2| at least 1e-4 below the limit, c2 normal) and those
+    that surely do not, from the oracle's fp64 terms; [nqb, nkb, 2] each."""
+    nqb, nkb = -(-n // 128), -(-n // 64)
+    sm = O.default_sm_scale(d)
+    bias = O.q_smooth_bias(quant["q_mean"][b, h], k_head, quant["k_mean"][b, h], sm)
+    c2 = (quant["q_scale"][b, h].astype(np.float32)[:, None] * quant["k_scale"][b, h].astype(np.float32)[None, :])
+    c2 = (c2.astype(np.float32) * np.float32(LOG2E)).astype(np.float32).astype(np.float64)
+    normal = (c2 >= np.finfo(np.float32).tiny) & (c2 <= 3.0e38)
+    ratio = np.zeros((nqb, 64 * nkb))
+    keys = np.arange(n)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio[:, :n] = np.abs(bias) * float(LOG2E) / c2[:, keys // 64]
+    hmax = np.nan_to_num(ratio, nan=np.inf).reshape(nqb, nkb, 2, 32).max(axis=-1)
+    limit = (1 << 22) - 1 - 127 * 127 * d
+    sure_fit = normal[:, :, None] & (hmax < limit * (1 - 1e-4))
+    sure_fb = ~normal[:, :, None] | (hmax > limit * (1 + 1e-4))
+    return sure_fit, sure_fb
+
+
 def check_terms(wsn, offs, quant, k, B, H, n, d, causal, expect_fallback=None):
     """The workspace's smoothing terms against the oracle's (dense, H_kv = H)."""
     nqb, nkb = -(-n // 128), -(-n // 64)
@@ -313,12 +334,26 @@ def test_smooth_q_workload(name):
     say(f"case smooth_q workload {name} {w.description}")
     x = workloads.generate(w)
     B, H, N, d = x.q.shape
+    ws = torch.empty(sage.sage_attn_workspace_size(B, H, N, d, w.pv_mode, smooth_q=True), dtype=torch.uint8,
+                     device="cuda")
     o = host(sage.sage_attn_fwd(dev(x.q), dev(x.k), dev(x.v), is_causal=w.causal, pv_mode=w.pv_mode,
-                                smooth_q=True))
+                                smooth_q=True, workspace=ws))
     torch.cuda.synchronize()
+    offs = sage.sage_test_workspace_layout(False, B, H, N, 0, d, w.pv_mode, smooth_q=True)
+    nqb, nkb = -(-N // 128), -(-N // 64)
+    flags = host(ws[offs[10]:offs[10] + 4 * B * H * nqb * 2 * nkb]).view(np.int32).reshape(B, H, nqb, nkb, 2)
     rng = np.random.default_rng(w.seed + 9)
     heads = [(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))]
     ref = O.quant_qk_dense(x.q[:, :, :, :], x.k, smooth_q=True)
+    live = np.ones((nqb, nkb), bool)
+    if w.causal:
+        live = 64 * np.arange(nkb)[None, :] <= 128 * np.arange(nqb)[:, None] + 127
+    say(f"  fallback halves: {int(flags[:, :, live].sum())} of {B * H * int(live.sum()) * 2}")
+    for b, h in heads:
+        sure_fit, sure_fb = fit_decisions(ref, x.k[b, h], b, h, N, d)
+        got = flags[b, h]
+        assert (got[sure_fit & live[:, :, None]] == 0).all(), ("flag set on a fitting half", b, h)
+        assert (got[sure_fb & live[:, :, None]] == 1).all(), ("flag missing", b, h)
     vq = O.quant_v_fp8(x.v) if w.pv_mode == "fp8" else None
     for b, h in heads:
         rows = _sample_rows(N, rng)

@@ -32,7 +32,7 @@ def _head_inputs(w, h):
 
 
 @pytest.mark.parametrize("name", ["tiny", "llm_prefill", "video_dit", "video_dit_biasx20",
-                                  "long_fp8", "varlen", "seq16k"])
+                                  "long_fp8", "varlen", "seq16k", "seq16k_causal"])
 def test_method_vs_exact_at_workload_shape(name):
     w = workloads.get(name)
     h = 1

@@ -79,6 +79,8 @@ WORKLOADS = {
                  description="16 packed sequences, lengths U[512,8192], H=32,d=128 causal, fp16 PV"),
         Workload("seq16k", 6, 1, 40, 16384, 128, False, "fp16", k_bias=3.0,
                  description="B=1,H=40,N=16384,d=128 non-causal, fp16 PV (16K, d=128 point)"),
+        Workload("seq16k_causal", 7, 1, 40, 16384, 128, True, "fp16", k_bias=3.0,
+                 description="B=1,H=40,N=16384,d=128 causal, fp16 PV (the 16K point's causal variant)"),
     ]
 }
 
