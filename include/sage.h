@@ -214,7 +214,9 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  *   [B,H,nqb,2·nkb] (nqb = ceil(N/128), nkb = ceil(N/64), npad = 64·nkb;
  *   entry [.,.,b,2t+s] = 1 where half s of key tile t carries the term in
  *   fp32 — then [9] holds it, as sm_scale·q̄_b·x_j·log2(e) — else [8] holds
- *   1.5·2^23 bits + rint(that / (δQ_b·δK_t·log2 e))), [11] total size
+ *   1.5·2^23 bits + rint(that / (δQ_b·δK_t·log2 e)); the flags are followed, at
+ *   the next 16-byte boundary, by one int32 per (b, h, Q block), nonzero when
+ *   some half of that block's row falls back), [11] total size
  *   (internal scratch sits between [6] and [7]).
  *   With SAGE_MXFP4 the regions are instead [0] Q e2m1 codes [rows][d/2]
  *   (channel c in nibble c%2 of byte c/2), [1] the smoothed K's codes, [2] Q

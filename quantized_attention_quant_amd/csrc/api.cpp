@@ -18,6 +18,12 @@ constexpr size_t kWsAlign = 256;
 constexpr int64_t kMaxTokensPerSeq = int64_t(1) << 23;  // keeps the int64 fixed-point K sums exact
 
 inline size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+inline size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+// The per-row fallback summaries follow the flags inside region [11].
+inline int32_t* row_summaries(char* flags, int B, int H, int N) {
+  const size_t qblocks = (size_t)B * H * ceil_div64(N, sage::kQBlock);
+  return reinterpret_cast<int32_t*>(flags + align16(sizeof(int32_t) * qblocks * (size_t)(2 * ceil_div64(N, sage::kKBlock))));
+}
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool debug_sync() {
   static const bool on = [] {
@@ -80,7 +86,8 @@ WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d
       sq * sizeof(float) * qblocks * d,
       sq * sizeof(int32_t) * qblocks * (size_t)(nkb * sage::kKBlock),
       sq * sizeof(float) * qblocks * (size_t)(nkb * sage::kKBlock),
-      sq * sizeof(int32_t) * qblocks * (size_t)(2 * nkb),
+      // fallback flags, then (16-byte aligned) the per-row summaries
+      sq * (align16(sizeof(int32_t) * qblocks * (size_t)(2 * nkb)) + align16(sizeof(int32_t) * qblocks)),
   };
   WsLayout L;
   size_t cur = 0;
@@ -188,7 +195,8 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
     if (sq) {
       // q̄·x in raw score units: the kernel applies the softmax scale to the sum
       sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, nullptr, qm, nullptr,
-                         reinterpret_cast<int32_t*>(terms), nullptr, nullptr, g, g.H / Hkv, 1.0f, is_causal != 0};
+                         reinterpret_cast<int32_t*>(terms), nullptr, nullptr, nullptr, g, g.H / Hkv, 1.0f,
+                         is_causal != 0};
       qa.raw = 1;
       sage::launch_q_bias(qa, st);
     }
@@ -213,8 +221,10 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.off[11]);
 
   sage::launch_quant_qk(g, gk, q, k, sm, q8, k8, qs, ks, km, qm, qtok, colsum, st);
+  int32_t* any = sq ? row_summaries(ws + L.off[11], g.B, g.H, g.N) : nullptr;
   if (sq) {
-    const sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, ks, qm, qs, slots, fix, flags, g, g.H / Hkv,
+    sage::launch_zero(any, align16(sizeof(int32_t) * (size_t)g.B * g.H * ceil_div64(g.N, sage::kQBlock)), st);
+    const sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, ks, qm, qs, slots, fix, flags, any, g, g.H / Hkv,
                              (float)((double)sm * 1.4426950408889634), is_causal != 0};
     sage::launch_q_bias(qa, st);
   }
@@ -226,6 +236,7 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
     a.qb_slots = slots;
     a.qb_fix = fix;
     a.qb_flags = flags;
+    a.qb_any = any;
   }
   sage::launch_attn(a, is_causal != 0, fp8, st);
   return finish(st);
@@ -410,6 +421,7 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
     a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[9]);
     a.qb_fix = reinterpret_cast<const float*>(ws + L.off[10]);
     a.qb_flags = reinterpret_cast<const int32_t*>(ws + L.off[11]);
+    a.qb_any = row_summaries(const_cast<char*>(ws) + L.off[11], B, H, N);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   sage::launch_attn(a, is_causal != 0, fp8, st);

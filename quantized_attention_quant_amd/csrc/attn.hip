@@ -177,6 +177,9 @@ __device__ __forceinline__ void wait_dma_and_sync() {
 __device__ __forceinline__ float load_uniform(const float* p, int64_t i) {
   return ((const __attribute__((address_space(4))) float*)p)[i];
 }
+__device__ __forceinline__ int load_uniform_i(const int32_t* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) int32_t*)p)[i];
+}
 typedef int v2i __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ v2i load_uniform2(const int32_t* p, int64_t i) {  // i even
   return ((const __attribute__((address_space(4))) v2i*)p)[i / 2];
@@ -551,6 +554,7 @@ void attn_fwd_kernel(AttnArgs a) {
   // q0/128 and, if it exists, the next), fallback flags and fp32 terms
   const int npad = nkb * kKBlock;
   const int wqb = wq_lo / kQBlock;  // this wave's Q block
+  const int wqb_in = min(wqb, nqb - 1);  // the same, kept in range for waves past n
   SlotSrc ss{};
   if (SM) ss = SlotSrc{a.qb_slots + (hs * nqb + q0 / kQBlock) * (int64_t)npad, (q0 + kQBlock < n ? 2 : 1) * npad * 4,
                        npad};
@@ -559,8 +563,11 @@ void attn_fwd_kernel(AttnArgs a) {
   load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
   // δQ: the wave's block scale (uniform), or this lane's query's own scale
   const float dq = QM == kQmToken ? (qrow < n ? a.q_scale[row0 + qrow] : 0.f)
-                                  : load_uniform(a.q_scale, hs * nqb + wq_lo / kQBlock);
+                                  : load_uniform(a.q_scale, hs * nqb + wqb_in);
   const float* __restrict__ ksc = a.k_scale + hsk * nkb;
+  // smoothed Q: whether any half tile of this wave's Q block falls back (rare);
+  // only then are the per-tile flags read
+  const bool row_fb = SM && load_uniform_i(a.qb_any, hs * nqb + wqb_in) != 0;
   c.m_run = -__builtin_inff();
   c.l_run = 0.f;
 #pragma unroll
@@ -592,7 +599,7 @@ void attn_fwd_kernel(AttnArgs a) {
       const bool full = (k0 + kKBlock <= n) && (!CAUSAL || k0 + kKBlock - 1 <= wq_lo);
       if (!full) mask_scores<CAUSAL>(c.S, k0, n, qrow, gg);
       float M = kMagicF;
-      if (SM) {
+      if (SM && row_fb) {
         const int64_t row = hs * nqb + wqb;
         const v2i fb = load_uniform2(a.qb_flags, row * (2 * nkb) + 2 * u);
         if (fb.x | fb.y) {

@@ -19,10 +19,12 @@ struct AttnArgs {
   int kv_group;            // query heads per K/V head: K/V head of h is h / kv_group
   // smoothed Q (all nullptr otherwise): per (Q block, key) accumulator initial
   // values [B][H][nqb][npad], per (Q block, tile, half) fallback flags
-  // [B][H][nqb][2*nkb] and fp32 terms [B][H][nqb][npad] (npad = 64*nkb)
+  // [B][H][nqb][2*nkb], fp32 terms [B][H][nqb][npad] (npad = 64*nkb) and per
+  // (Q block) row summaries [B][H][nqb] (nonzero: some half of the row falls back)
   const int32_t* qb_slots = nullptr;
   const float* qb_fix = nullptr;
   const int32_t* qb_flags = nullptr;
+  const int32_t* qb_any = nullptr;
   bool q_per_token = false;  // q_scale holds one scale per query row
 };
 
@@ -51,6 +53,7 @@ struct QBiasArgs {
   int32_t* slots;          // [B][H][nqb][npad]
   float* fix;              // [B][H][nqb][npad]
   int32_t* flags;          // [B][H][nqb][2*nkb]
+  int32_t* any;            // [B][H][nqb], zero on entry: set where a half of the row falls back
   SeqGeom g;               // geometry of Q (H query heads)
   int kv_group;
   float sm_log2e;          // softmax scale times log2(e)

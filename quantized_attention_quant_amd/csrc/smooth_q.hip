@@ -21,7 +21,9 @@
 //     or whose c is not a normal float (δQ = 0 for a constant block), gets the
 //     bias alone and
 //   flags[hs][b][2t + s] = 1 (half s of tile t), with fix[hs][b][j] = Δ·log2e
-//     (fp32) for its keys: the attention kernel then adds Δ in fp32.
+//     (fp32) for its keys: the attention kernel then adds Δ in fp32.  any[hs][b]
+//     (cleared before the launch) becomes nonzero when some half of block b
+//     falls back, so the attention kernel reads the flags of that row only.
 //
 // MXFP4 (raw): the scores accumulate in fp32, so the term needs no integer
 // form: slots[hs][b][j] holds q̄_b · x_j itself (fp32 bits, raw score units,
@@ -248,7 +250,10 @@ __global__ __launch_bounds__(kThreads) void q_bias_kernel(QBiasArgs a) {
               *reinterpret_cast<float4*>(a.fix + rowoff + key0) =
                   float4{dl[4 * q4], dl[4 * q4 + 1], dl[4 * q4 + 2], dl[4 * q4 + 3]};
           }
-          if (gg == 0) a.flags[(hs * nqb + bb) * (int64_t)(2 * nkb) + 2 * t + s] = fits ? 0 : 1;
+          if (gg == 0) {
+            a.flags[(hs * nqb + bb) * (int64_t)(2 * nkb) + 2 * t + s] = fits ? 0 : 1;
+            if (!fits) atomicOr(a.any + hs * nqb + bb, 1);  // the row's summary (rare)
+          }
         }
       }
     }

@@ -125,6 +125,15 @@ def check_terms(wsn, offs, quant, k, B, H, n, d, causal, expect_fallback=None):
     slots = wsn[offs[8]:offs[8] + 4 * B * H * nqb * npad].view(np.int32).reshape(B, H, nqb, npad)
     fix = wsn[offs[9]:offs[9] + 4 * B * H * nqb * npad].view(np.float32).reshape(B, H, nqb, npad)
     flags = wsn[offs[10]:offs[10] + 4 * B * H * nqb * 2 * nkb].view(np.int32).reshape(B, H, nqb, nkb, 2)
+    # per-row summaries after the flags (16-byte aligned): nonzero iff a written half falls back
+    so = offs[10] + -(-4 * B * H * nqb * 2 * nkb // 16) * 16
+    summary = wsn[so:so + 4 * B * H * nqb].view(np.int32).reshape(B, H, nqb)
+    live = np.ones((nqb, nkb), bool)
+    if causal:
+        live = 64 * np.arange(nkb)[None, :] <= 128 * np.arange(nqb)[:, None] + 127
+    for blk in range(nqb):
+        want_any = (flags[:, :, blk][:, :, live[blk]] != 0).any(axis=(2, 3))
+        assert ((summary[:, :, blk] != 0) == want_any).all(), ("row summary", blk)
     sm = O.default_sm_scale(d)
     seen_fb = 0
     for b in range(B):
