@@ -207,7 +207,8 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  * sage_test_workspace_layout: byte offsets, inside the sage_attn_fwd
  *   (varlen == 0) or sage_attn_varlen_fwd (varlen != 0) workspace, of
  *   [0] q_int8, [1] k_int8, [2] q_scale, [3] k_scale, [4] k_mean,
- *   [5] packed V, [6] v_scale (fp8 mode; an empty region in fp16 mode),
+ *   [5] packed e4m3 V and [6] v_scale (fp8 mode; both empty in fp16 mode, whose
+ *   kernel reads the caller's V directly),
  *   and, with SAGE_OPT_SMOOTH_Q (empty regions otherwise), [7] q_mean fp32
  *   [B,H,nqb,d], [8] accumulator initial values int32 [B,H,nqb,npad],
  *   [9] fp32 fallback terms [B,H,nqb,npad], [10] fallback flags int32
@@ -243,12 +244,14 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  * sage_test_attn_from_workspace: launch only the fused attention kernel on a
  *   workspace that a preceding sage_attn_fwd call with the same B,H,H_kv,N,d,
  *   is_causal, pv_mode and options has filled (its pre-pass results are reused as they
- *   are); writes o fp16 [B,H,N,d] (no LSE).  Used to time the attention
+ *   are); writes o fp16 [B,H,N,d] (no LSE).  v: that call's fp16 V
+ *   [B,H_kv,N,d] (SAGE_PV_FP16 reads it directly; ignored, may be NULL, in the
+ *   other modes).  Used to time the attention
  *   kernel alone.  Same validation as sage_attn_fwd.  SAGE_MXFP4 uses the
  *   default softmax scale.
  */
-sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int N, int d,
-                                            int is_causal, sage_pv_mode_t pv_mode, int options,
+sage_status_t sage_test_attn_from_workspace(void* o, const void* v, int B, int H, int H_kv, int N,
+                                            int d, int is_causal, sage_pv_mode_t pv_mode, int options,
                                             const void* workspace, size_t workspace_bytes,
                                             sage_stream_t stream);
 sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int N,

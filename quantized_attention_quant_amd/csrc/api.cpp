@@ -34,7 +34,7 @@ inline bool debug_sync() {
 }
 
 // Offsets inside the attention workspace:
-// [0] q_int8 [1] k_int8 [2] q_scale [3] k_scale [4] k_mean [5] packed V
+// [0] q_int8 [1] k_int8 [2] q_scale [3] k_scale [4] k_mean [5] packed V (fp8)
 // [6] v_scale (fp8) [7] int64 K column sums; with a smoothed Q [8] q_mean,
 // [9] accumulator initial values, [10] fp32 fallback terms, [11] fallback
 // flags; total returned separately.
@@ -80,7 +80,7 @@ WsLayout make_layout(bool varlen, int B, int H, int Hkv, int N, int64_t T, int d
       sizeof(float) * (q_per_token ? (size_t)tokens : (size_t)B * H * nqb),
       sizeof(float) * (size_t)B * Hkv * nkb,
       sizeof(float) * (size_t)B * Hkv * d,
-      (size_t)vtiles * sage::kKBlock * d * (fp8 ? 1 : 2),
+      fp8 ? (size_t)vtiles * sage::kKBlock * d : 0,  // FP16 PV reads the input V itself
       fp8 ? sizeof(float) * (size_t)B * Hkv * d : 0,
       sizeof(long long) * (size_t)B * Hkv * d,
       sq * sizeof(float) * qblocks * d,
@@ -228,9 +228,13 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
                              (float)((double)sm * 1.4426950408889634), is_causal != 0};
     sage::launch_q_bias(qa, st);
   }
-  if (fp8) sage::launch_v_scale(gk, v, vs, st);
-  sage::launch_v_prepare(gk, v, vs, fp8, /*rowmajor=*/false, vp, st);
-  sage::AttnArgs a{q8, k8, qs, ks, vp, vs, static_cast<uint16_t*>(o), lse, g, g.H / Hkv};
+  if (fp8) {
+    sage::launch_v_scale(gk, v, vs, st);
+    sage::launch_v_prepare(gk, v, vs, /*fp8=*/true, /*rowmajor=*/false, vp, st);
+  }
+  // FP16 PV: the kernel reads V's fp16 rows directly (no copy)
+  sage::AttnArgs a{q8, k8, qs, ks, fp8 ? vp : static_cast<const uint8_t*>(v), vs, static_cast<uint16_t*>(o), lse, g,
+                   g.H / Hkv};
   a.q_per_token = qtok;
   if (sq) {
     a.qb_slots = slots;
@@ -383,15 +387,16 @@ sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int
   return SAGE_OK;
 }
 
-sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int N, int d, int is_causal,
-                                            sage_pv_mode_t pv_mode, int options, const void* workspace,
-                                            size_t workspace_bytes, sage_stream_t stream) {
+sage_status_t sage_test_attn_from_workspace(void* o, const void* v, int B, int H, int H_kv, int N, int d,
+                                            int is_causal, sage_pv_mode_t pv_mode, int options,
+                                            const void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   const sage_status_t s = check_dims(B, H, N, d);
   if (s != SAGE_OK) return s;
   if (!kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!o || !workspace || !aligned16(o) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
     return SAGE_ERR_INVALID_ARGUMENT;
   if (!pv_mode_ok(pv_mode)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv_mode == SAGE_PV_FP16 && (!v || !aligned16(v))) return SAGE_ERR_INVALID_ARGUMENT;
   if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
@@ -399,6 +404,8 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const size_t tensor_bytes = (size_t)B * H * N * d * 2;
   if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv_mode == SAGE_PV_FP16 && overlaps(o, tensor_bytes, v, tensor_bytes / (size_t)H * (size_t)H_kv))
+    return SAGE_ERR_INVALID_ARGUMENT;
   const char* ws = static_cast<const char*>(workspace);
   const SeqGeom g{nullptr, B, H, N, d, 0};
   if (pv_mode == SAGE_MXFP4) {
@@ -414,8 +421,8 @@ sage_status_t sage_test_attn_from_workspace(void* o, int B, int H, int H_kv, int
   }
   sage::AttnArgs a{reinterpret_cast<const int8_t*>(ws + L.off[0]), reinterpret_cast<const int8_t*>(ws + L.off[1]),
                    reinterpret_cast<const float*>(ws + L.off[2]), reinterpret_cast<const float*>(ws + L.off[3]),
-                   reinterpret_cast<const uint8_t*>(ws + L.off[5]), reinterpret_cast<const float*>(ws + L.off[6]),
-                   static_cast<uint16_t*>(o), nullptr, g, H / H_kv};
+                   fp8 ? reinterpret_cast<const uint8_t*>(ws + L.off[5]) : static_cast<const uint8_t*>(v),
+                   reinterpret_cast<const float*>(ws + L.off[6]), static_cast<uint16_t*>(o), nullptr, g, H / H_kv};
   a.q_per_token = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
   if (options & SAGE_OPT_SMOOTH_Q) {
     a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[9]);

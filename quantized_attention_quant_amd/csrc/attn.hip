@@ -60,14 +60,14 @@ constexpr float kLazyLimit = 256.0f;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-// One LDS stage: K̂ tile, packed V tile and, with a smoothed Q, the
+// One LDS stage: K̂ tile, V tile (FP16 PV: the input's rows; FP8: packed e4m3) and, with a smoothed Q, the
 // accumulator initial values of the tile's 64 keys for the workgroup's two Q
 // blocks (four 256-byte quarters: quarter w holds block w/2, keys 32(w%2) ..
 // +31 in its first 128 bytes).
 template <int D, bool FP8, int NT = kThreads, bool SM = false>
 struct TileGeom {
   static constexpr int KBYTES = kKBlock * D;                    // K̂ tile, int8
-  static constexpr int VBYTES = kKBlock * D * (FP8 ? 1 : 2);    // packed V tile
+  static constexpr int VBYTES = kKBlock * D * (FP8 ? 1 : 2);    // V tile
   static constexpr int SBYTES = SM ? 1024 : 0;                  // accumulator initial values
   static constexpr int KCHUNKS = KBYTES / 16;
   static constexpr int VCHUNKS = VBYTES / 16;
@@ -104,9 +104,52 @@ __device__ __forceinline__ int k_lds_chunk(int r, int c) {
   return r * KSwizzle<D>::CPR + KSwizzle<D>::chunk(r, c);
 }
 
+// FP16 PV reads V straight from the input's row-major rows ([key][d], 2D bytes
+// per key).  In 16-key block kc the PV A operand needs, per lane l, channel
+// 32dt + l%32 of keys 16kc + 4(l/32) + 0..3 and 16kc + 8 + 4(l/32) + 0..3 (the
+// key order in which the Sᵀ accumulator hands P to the B operand).  gfx950's
+// transposing LDS read (ds_read_b64_tr_b16) gathers four such keys: within
+// each 16-lane group, lane 4q + c receives element c of the 8-byte chunks that
+// lanes q, 4 + q, 8 + q, 12 + q address, in that order (probed on the
+// hardware).  So lane (g = l/16, j = (l/4)%4, q = l%4) addresses key row
+// 16kc + 8r + 4(g/2) + j (r = 0, 1: the two reads) at channels
+// 32dt + 16(g%2) + 4q .. +3.  The four rows a group reads share a bank line
+// (d = 128) or two (d = 64); XOR-ing the 16-byte chunk index with 2·(row % 4)
+// spreads the group's 16 chunks over 128 distinct bytes.
+__device__ __forceinline__ int v_lds_chunk16(int r, int c) { return c ^ (2 * (r & 3)); }
+
+typedef short v4s16 __attribute__((__vector_size__(8)));
+typedef short v8s16 __attribute__((__vector_size__(16)));
+typedef __attribute__((address_space(3))) v4s16* lds_v4s16_t;
+
+// One PV A-operand fragment from the tile's V rows in LDS: p is this lane's
+// address for the first four keys (the other four are 8 rows further on).
+__device__ __forceinline__ v8h v_frag_tr(const char* __restrict__ p, int row_bytes) {
+  const v4s16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16_t)p);
+  const v4s16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s16_t)(p + 8 * row_bytes));
+  return __builtin_bit_cast(v8h, (v8s16)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// This lane's two LDS byte offsets inside a V tile (even and odd 32-channel
+// steps): key row 4(g/2) + j, chunk (8·parity + 4(g%2) + q) ^ 4j in 8-byte units.
+template <int D>
+__device__ __forceinline__ void v_tr_bases(int lane, int& even, int& odd) {
+  const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+  const int row = 4 * (g >> 1) + j;
+  even = row * 2 * D + (((4 * (g & 1) + q) ^ (4 * j)) * 8);
+  odd = row * 2 * D + (((8 + 4 * (g & 1) + q) ^ (4 * j)) * 8);
+}
+
+// Fragment (kc, dt): 16-key block kc, 32-channel step dt.
+template <int D>
+__device__ __forceinline__ v8h v_frag(const char* __restrict__ vstage, int even, int odd, int kc, int dt) {
+  return v_frag_tr(vstage + (dt & 1 ? odd : even) + 16 * kc * 2 * D + 16 * (dt >> 1) * 8, 2 * D);
+}
+
 // Request K̂ tile t (rows 64t..64t+63 of the head-sequence, zeros past its end)
-// and packed V tile t into one LDS stage.  kbase/kbytes and vbase/vbytes bound
-// the head-sequence's K̂ rows and packed V tiles; reads past them return zero.
+// and V tile t into one LDS stage.  kbase/kbytes bound the head-sequence's K̂
+// rows; vbase/vbytes its fp16 V rows (FP16 PV, stored with the V swizzle) or
+// packed e4m3 tiles (FP8); reads past them return zero.
 // Lane i of a DMA instruction lands at the instruction's LDS base + 16·i, so
 // each lane fetches the global chunk that belongs at its swizzled position.
 template <int D, bool FP8, int NT = kThreads, bool SM = false>
@@ -131,8 +174,17 @@ __device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const 
 #pragma unroll
   for (int j = 0; j < G::VI; ++j) {
     const int base = (w * G::VI + j) * 64;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + base * 16), 16,
-                                             t * G::VBYTES + (base + lane) * 16, 0, 0, 0);
+    if (FP8) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + base * 16), 16,
+                                               t * G::VBYTES + (base + lane) * 16, 0, 0, 0);
+    } else {
+      constexpr int CPRV = D / 8;  // 16-byte chunks per fp16 row
+      const int p = base + lane;
+      const int r = p / CPRV;
+      const unsigned off = (unsigned)(t * kKBlock + r) * (2u * D) + 16u * v_lds_chunk16(r, p % CPRV);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + base * 16), 16, (int)off, 0, 0,
+                                               0);
+    }
   }
   if (SM) {
     // quarter w (w < 4): lanes 0-31 fetch block w/2, keys 64t + 32(w%2) + lane;
@@ -277,7 +329,8 @@ __device__ __forceinline__ float tile_max(float mx, float c2) {
 __device__ __forceinline__ float exp_pack_fp16(const float (&F)[2][16], float c2, float m_ref, v8h (&pk)[4],
                                                float M = kMagicF) {
   const float kb = __builtin_fmaf(M, c2, m_ref);
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  // -0 is the exact identity of addition, so the first add of each sum folds away
+  float part[4] = {-0.f, -0.f, -0.f, -0.f};
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
     const int s = kc >> 1, hh = kc & 1;
@@ -296,7 +349,7 @@ __device__ __forceinline__ float exp_pack_fp16(const float (&F)[2][16], float c2
 // F - mx exact (both in [2^23, 2^24)); p·448 <= 448·2^(2^-20) < 464, so the
 // conversion cannot overflow.  P is packed as one 32-byte B operand.
 __device__ __forceinline__ float exp_pack_fp8(const float (&F)[2][16], float mx, float c2, float cterm, v8i& pk) {
-  float lsum = 0.f;
+  float lsum = -0.f;
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int s = q >> 2, i0 = 4 * (q & 3);
@@ -319,12 +372,13 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ vstage, int lan
                                         const v8i& pk8, v16f (&O)[D / 32]) {
   constexpr int DT = D / 32;
   if (!FP8) {
-    const v8h* lv = reinterpret_cast<const v8h*>(vstage);
+    int ve, vo;
+    v_tr_bases<D>(lane, ve, vo);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(lv[(kc * DT + dt) * 64 + lane], pk16[kc], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_frag<D>(vstage, ve, vo, kc, dt), pk16[kc], O[dt], 0, 0, 0);
   } else {
     const v8i* lv = reinterpret_cast<const v8i*>(vstage);
 #pragma unroll
@@ -335,8 +389,9 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ vstage, int lan
 
 // Matrix phase with both parts (the steady state): PV of the previous tile and
 // QKᵀ of the current one in one scheduling region.  All K̂ fragment reads go
-// first; then every MFMA is followed by one V fragment read while any remain,
-// so each LDS read has several MFMAs (>= 256 cycles) to land before its use.
+// first; then every MFMA is followed by one V fragment read (two 64-bit
+// transposing reads for FP16) while any remain, so each LDS read has several
+// MFMAs (>= 256 cycles) to land before its use.
 template <int D, bool FP8, bool SM = false>
 __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, const char* __restrict__ vstage,
                                             int lane, int r32, int gg, const v4i (&qf)[D / 32], v16i (&S)[2],
@@ -344,16 +399,18 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
                                             const v4i* __restrict__ lslots = nullptr) {
   constexpr int DT = D / 32;
   constexpr int NK = 2 * DT + (SM ? 8 : 0);  // K̂ fragment (+ initial value) reads (128-bit)
-  constexpr int NV = FP8 ? 2 * DT : 4 * DT;  // V fragment reads (128-bit)
+  constexpr int NV = FP8 ? 2 * DT : 8 * DT;  // V fragment reads (FP8: 128-bit; FP16: 64-bit transposing)
+  constexpr int RPM = FP8 ? 1 : 2;           // V reads placed after each MFMA
   constexpr int NQK = 2 * DT;                // QKᵀ MFMAs
   constexpr int NPV = FP8 ? DT : 4 * DT;     // PV MFMAs
   v4i kf[2][DT];
   load_k_frags<D>(reinterpret_cast<const v4i*>(kstage), kf, r32, gg);
   if (!FP8) {
-    const v8h* lv = reinterpret_cast<const v8h*>(vstage);
+    int ve, vo;
+    v_tr_bases<D>(lane, ve, vo);
     v8h vf[4 * DT];
 #pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) vf[i] = lv[i * 64 + lane];
+    for (int i = 0; i < 4 * DT; ++i) vf[i] = v_frag<D>(vstage, ve, vo, i / DT, i % DT);
     qk_half<D, SM>(kf, qf, S, lslots, gg);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
@@ -375,7 +432,7 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
 #pragma unroll
   for (int i = 0; i < NQK + NPV; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < NV) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (i < NV / RPM) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);
   }
 }
 
@@ -547,8 +604,9 @@ void attn_fwd_kernel(AttnArgs a) {
   const int ntiles = ceil_div(kend, kKBlock);
   const int8_t* kbase = a.k + krow0 * D;
   const int kbytes = n * D;
-  const uint8_t* vbase = a.v_packed + vtile_index(gk, b, hk, 0) * G::VBYTES;
-  const int vbytes = ceil_div(n, kKBlock) * G::VBYTES;
+  // V: FP16 PV reads the input's rows of this head-sequence; FP8 its packed tiles
+  const uint8_t* vbase = FP8 ? a.v + vtile_index(gk, b, hk, 0) * G::VBYTES : a.v + krow0 * D * 2;
+  const int vbytes = FP8 ? ceil_div(n, kKBlock) * G::VBYTES : (int)((unsigned)n * 2u * D);
   constexpr int L = G::KI + G::VI + G::SI;  // DMA instructions per group-A wave per tile
   // smoothed Q: this workgroup's rows of accumulator initial values (Q blocks
   // q0/128 and, if it exists, the next), fallback flags and fp32 terms
@@ -905,7 +963,7 @@ __device__ __forceinline__ void mx_softmax(MxWave<D>& c, float c2) {
     for (int j = 0; j < 8; ++j) p[q][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[q >> 1][8 * (q & 1) + j], c2, -m_new));
   __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);   // the FMAs
   __builtin_amdgcn_sched_group_barrier(0x400, 32, 0);   // the exponentials
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  float part[4] = {-0.f, -0.f, -0.f, -0.f};
   uint32_t w[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {

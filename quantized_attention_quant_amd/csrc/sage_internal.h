@@ -11,7 +11,7 @@ struct AttnArgs {
   const int8_t* k;         // K codes (H / kv_group heads)
   const float* q_scale;    // [B][H][nqb] (per token: indexed like the Q rows), softmax scale folded in
   const float* k_scale;    // [B][Hkv][nkb]
-  const uint8_t* v_packed; // packed V tiles (fp16 or e4m3), Hkv heads
+  const uint8_t* v;        // FP16 PV: the fp16 input V itself; FP8: packed e4m3 tiles (Hkv heads)
   const float* v_scale;    // [B][Hkv][d] (FP8 mode)
   uint16_t* o;             // fp16 output, same layout as the input
   float* lse;              // optional fp32 log-sum-exp per query row, or nullptr
