@@ -316,7 +316,8 @@ def main():
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / reps
         achieved = ops / (kern_ms * 1e-3) / 1e12
-        traffic = measured_traffic(w.name + ("+smooth_q" if sq else "") + ("+q_per_token" if qt else ""))
+        traffic = measured_traffic(w.name + ("+mxfp4" if w.pv_mode == "mxfp4" else "") + ("+smooth_q" if sq else "")
+                                   + ("+q_per_token" if qt else ""))
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
                     "kernel": f"{'attn_mx_kernel' if w.pv_mode == 'mxfp4' else 'attn_fwd_kernel'}<{w.d},{w.pv_mode}"
