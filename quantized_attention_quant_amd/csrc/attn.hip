@@ -329,19 +329,24 @@ __device__ __forceinline__ float tile_max(float mx, float c2) {
 __device__ __forceinline__ float exp_pack_fp16(const float (&F)[2][16], float c2, float m_ref, v8h (&pk)[4],
                                                float M = kMagicF) {
   const float kb = __builtin_fmaf(M, c2, m_ref);
-  // -0 is the exact identity of addition, so the first add of each sum folds away
-  float part[4] = {-0.f, -0.f, -0.f, -0.f};
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
     const int s = kc >> 1, hh = kc & 1;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(F[s][8 * hh + j], c2, -kb));
-      part[kc] += p;
       pk[kc][j] = (_Float16)p;
     }
   }
-  return (part[0] + part[1]) + (part[2] + part[3]);
+  // The lane's share of the row sum, from the fp16 P that enters the PV product:
+  // a pairwise tree of packed fp16 adds (15 v_pk_add_f16 instead of 28 fp32
+  // adds; four fp16 roundings, so within 4·2^-11 of the exact sum of the fp16
+  // values; p <= 2^8 on an accepted tile keeps it far from fp16 overflow, and
+  // an overflowing first pass gives inf, which fails the lazy check below).
+  const v8h s8 = (pk[0] + pk[1]) + (pk[2] + pk[3]);
+  const v4h s4 = __builtin_shufflevector(s8, s8, 0, 1, 2, 3) + __builtin_shufflevector(s8, s8, 4, 5, 6, 7);
+  const v2h s2 = __builtin_shufflevector(s4, s4, 0, 1) + __builtin_shufflevector(s4, s4, 2, 3);
+  return (float)s2[0] + (float)s2[1];
 }
 
 // FP8 PV: the e4m3 codes of 448·p follow the running max itself (the schedule

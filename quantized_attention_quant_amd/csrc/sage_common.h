@@ -21,6 +21,7 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 
 // One "head-sequence": a (batch entry, head) of a dense [B,H,N,d] tensor or a
 // (sequence, head) of a packed [H,T,d] tensor.  Everything the method does per
