@@ -81,6 +81,8 @@ WORKLOADS = {
                  description="B=1,H=40,N=16384,d=128 non-causal, fp16 PV (16K, d=128 point)"),
         Workload("seq16k_causal", 7, 1, 40, 16384, 128, True, "fp16", k_bias=3.0,
                  description="B=1,H=40,N=16384,d=128 causal, fp16 PV (the 16K point's causal variant)"),
+        Workload("long_fp8_shard8", 8, 1, 5, 32768, 128, False, "fp8", q_bias=3.0, k_bias=3.0,
+                 description="one GPU's head share of long_fp8 on 8 GPUs: B=1,H=5,N=32768,d=128, FP8 PV"),
     ]
 }
 
