@@ -1,0 +1,92 @@
+"""The largest sequence the ABI accepts: one causal head of 2^23 - 37 tokens
+at d = 128.  There the fp16 V rows the kernel streams span just under 2^31
+bytes and the K̂ rows 2^30, so every 32-bit offset and buffer range in the
+pre-pass and the attention kernel is near its limit.
+
+Inputs: a seeded 2^18-row block (the workload generator's distributions,
+K bias N(0,3)) repeated to length, plus a small deterministic per-row
+perturbation (period 997 rows), so that every row differs and a read from
+the wrong repetition would show in the outputs.
+
+Checks: K mean, all K̂ codes and scales, and Q̂ codes and scales of the
+sampled rows' blocks bit-exact against the oracle; sampled output rows (the
+first, the last, and rows past 2^20 and 2^22) within the parity bar of the
+oracle's method.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import quantized_attention_quant_amd as sage
+import workloads
+from oracle import sage_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+COS_O1 = 0.9995
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _inputs(N, d, P=1 << 18):
+    base = workloads.generate_custom(990, 1, 1, P, d, k_bias=3.0)
+    reps = -(-N // P)
+    r = np.arange(N, dtype=np.int64)
+    pert = (((r % 997) - 498).astype(np.float32) / np.float32(4096.0))[:, None]
+    out = []
+    for a, s in ((base.q, 1.0), (base.k, 2.0), (base.v, 4.0)):
+        t = np.tile(a[0, 0], (reps, 1))[:N].astype(np.float32)
+        t += pert * np.float32(s)
+        out.append(t.astype(np.float16)[None, None])
+        del t
+    return out
+
+
+def test_max_sequence_causal_fp16():
+    N, d = (1 << 23) - 37, 128
+    say(f"case max size N={N} d={d} causal fp16")
+    q, k, v = _inputs(N, d)
+    say("  inputs ready")
+    qd, kd, vd = (torch.from_numpy(a).cuda() for a in (q, k, v))
+    got = sage.sage_quant_qk(qd, kd)
+    o = sage.sage_attn_fwd(qd, kd, vd, is_causal=True, pv_mode="fp16")
+    torch.cuda.synchronize()
+    say("  GPU done")
+    # K: mean, every code and scale
+    kc, ks, km = O.quant_k(k[0, 0])
+    assert (host(got["k_mean"])[0, 0].view(np.uint32) == km.view(np.uint32)).all(), "k_mean"
+    assert (host(got["k_scale"])[0, 0].view(np.uint32) == ks.view(np.uint32)).all(), "k_scale"
+    assert np.array_equal(host(got["k_int8"])[0, 0], kc), "k_int8"
+    say("  K codes, scales and mean bit-exact")
+    rows = np.array([0, 1, 127, 128, (1 << 20) + 5, (1 << 22) + 77, N - 2, N - 1])
+    sm = O.default_sm_scale(d)
+    # Q: the sampled rows' blocks (Q blocks are independent)
+    qi_all = host(got["q_int8"])[0, 0]
+    qs_all = host(got["q_scale"])[0, 0]
+    nqb = -(-N // 128)
+    qc = np.zeros((N, d), np.int8)
+    qs = np.zeros(nqb, np.float32)
+    for blk in sorted({int(r) // 128 for r in rows}):
+        a, b = 128 * blk, min(N, 128 * blk + 128)
+        c, s = O.quant_q(q[0, 0, a:b], sm)
+        assert np.array_equal(qi_all[a:b], c), ("q_int8", blk)
+        assert qs_all[blk].view(np.uint32) == s[0].view(np.uint32), ("q_scale", blk)
+        qc[a:b], qs[blk] = c, s[0]
+    say("  sampled Q blocks bit-exact")
+    o1 = O.sage_attention_rows(qc, qs, kc, ks, v[0, 0], rows, True, "fp16")
+    ours = host(o[0, 0, torch.from_numpy(rows).cuda()]).astype(np.float64)
+    err = np.abs(ours - o1).max()
+    c1 = float((ours.ravel() @ o1.ravel()) / (np.linalg.norm(ours) * np.linalg.norm(o1)))
+    say(f"  sampled rows: max_abs_vs_O1={err:.3e} cos_O1={c1:.6f}")
+    assert np.isfinite(ours).all()
+    assert err <= MAX_ABS and c1 >= COS_O1, (err, c1)
+
+
+def host(t):
+    return t.cpu().numpy()
