@@ -321,11 +321,15 @@ __device__ __forceinline__ float tile_max(float mx, float c2) {
 }
 
 // FP16 PV: p = 2^(F·c - K), K = fl(M·c + m_ref) — one FMA per score, M the
-// bias of F (1.5·2^23, or 0 for scores already in log2 units).  The rounding
-// of K shifts a row-tile's exponents by <= ulp(K)/2, a common factor on its p
-// and on its share of l.  P is packed as four B operands; the returned
-// row-tile sum is over the unrounded p, in fp32 adds (dot instructions would
-// share the matrix pipeline and stall behind the other wave's MFMAs).
+// bias of F (1.5·2^23, or 0 for scores already in log2 units).  Rounding K
+// moves the tile's exponents by up to ulp(K)/2 ≈ 0.75·c (log2 units) against
+// the reference the other tiles use, i.e. a relative weight error of up to
+// ~0.5·c for the tile: at most 0.4 % while c < kExactC2 = 2^-7 (ordinary
+// inputs: c from 1e-4 to 5e-3).  Tiles with a larger c (|q|·|k| in the
+// hundreds or more) are first taken to exact log2 units, (F - M)·c with F - M
+// the integer score, and come here with c = 1, M = 0.  P is packed as four B
+// operands.
+constexpr float kExactC2 = 1.0f / 128.0f;
 __device__ __forceinline__ float exp_pack_fp16(const float (&F)[2][16], float c2, float m_ref, v8h (&pk)[4],
                                                float M = kMagicF) {
   const float kb = __builtin_fmaf(M, c2, m_ref);
@@ -641,6 +645,18 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) c.O[dt][i] = 0.f;
 
+  // FP16: the largest δK of the tiles this workgroup reads (four independent
+  // loads per lane and pass; 256 tiles, the 16K case, take one pass)
+  float dkmax = 0.f;
+  if (!FP8) {
+    for (int i0 = lane; i0 < ntiles; i0 += 256) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = (i0 + 64 * j < ntiles) ? ksc[i0 + 64 * j] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dkmax = __builtin_fmaxf(dkmax, v[j]);
+    }
+  }
   if (lead) {
     const int first = min(kAhead, ntiles);
     for (int t = 0; t < first; ++t)
@@ -650,6 +666,9 @@ void attn_fwd_kernel(AttnArgs a) {
   // here also lets the compiler see that no later MFMA waits on the Q̂ loads
   wait_dma<0>();
   barrier_only();
+  // FP16: can a tile's factor δQ·δK·log2(e) exceed kExactC2 in this wave?
+  // Only then are its tiles checked one by one (rare inputs).
+  const bool exact_wave = !FP8 && __any(dq * wave_max(dkmax) * kLog2e > kExactC2);
 
   // tiles this wave takes part in: 0..nact-1 (causal: keys up to its last query)
   const int nact = !wave_rows ? 0 : CAUSAL ? min(ntiles, wq_hi / kKBlock + 1) : ntiles;
@@ -690,7 +709,24 @@ void attn_fwd_kernel(AttnArgs a) {
           M = 0.f;
         }
       }
-      softmax_phase<D, FP8, SM>(c, c2, M);
+      if (exact_wave && M != 0.f && __any(c2 > kExactC2)) {
+        // a large factor (rare inputs): the scores to exact log2 units in
+        // place, (F - M)·c2, and the softmax runs with c2 = 1, M = 0; the
+        // laundered M keeps the conversion inside this branch
+        float mz = kMagicF;
+        asm volatile("" : "+v"(mz));
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int bits = c.S[s][i];
+            c.S[s][i] = __float_as_int((__int_as_float(bits) - mz) * c2);
+          }
+        c2 = 1.f;
+        M = 0.f;
+      }
+      // FP16 takes the scores' bias at run time (magic-biased, or log2 units)
+      softmax_phase<D, FP8, SM || !FP8>(c, c2, M);
     }
   };
   // One workgroup barrier per tile.  Group A runs matrix(t) then softmax(t),

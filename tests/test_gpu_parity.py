@@ -340,6 +340,37 @@ def test_varlen_small_all_rows():
 
 
 # ---------------------------------------------------------------------------
+# Large magnitudes: with |q|·|k| in the hundreds the per-tile factor
+# c = δQ·δK·log2(e) grows past 2^-7, where the FP16 path takes its scores to
+# exact log2 units before the softmax; every row against the method.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("scale", [8.0, 30.0])
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_large_magnitude_inputs(scale, pv_mode, d, causal):
+    say(f"case large magnitude x{scale} pv={pv_mode} d={d} causal={causal}")
+    B, H, n = 1, 2, 300
+    x = workloads.generate_custom(555 + d, B, H, n, d, k_bias=3.0, q_bias=1.0)
+    q = (x.q.astype(np.float32) * np.float32(scale)).astype(np.float16)
+    k = (x.k.astype(np.float32) * np.float32(scale)).astype(np.float16)
+    o = host(sage.sage_attn_fwd(dev(q), dev(k), dev(x.v), is_causal=causal, pv_mode=pv_mode))
+    quant = O.quant_qk_dense(q, k)
+    c2 = float(quant["q_scale"].max()) * float(quant["k_scale"].max()) * 1.4426950408889634
+    assert c2 > 2.0 ** -7, c2  # the inputs do reach the exact-conversion range
+    rows = np.arange(n)
+    for h in range(H):
+        qi, qs, ki, ks = O.head_views_dense(quant, 0, h)
+        if pv_mode == "fp8":
+            vc, vs = O.quant_v_fp8(x.v[0, h])
+            o1 = O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs)
+        else:
+            o1 = O.sage_attention_rows(qi, qs, ki, ks, x.v[0, h], rows, causal, "fp16")
+        o2 = O.sdpa_fp64_rows(q[0, h], k[0, h], x.v[0, h], rows, causal)
+        check_out(o[0, h], o1, o2, f"x{scale} {pv_mode} d={d} h={h}", min(COS_O2, cos(o1, o2) - 1e-4))
+
+
+# ---------------------------------------------------------------------------
 # Full-size workloads: whole-tensor bit-exact quantisation, sampled output rows
 # ---------------------------------------------------------------------------
 def _sample_rows(n, rng, k=48):
