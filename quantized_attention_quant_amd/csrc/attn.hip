@@ -26,10 +26,11 @@
 //     |Q̂K̂ᵀ| <= 128·127² < 2^22, the result read as fp32 is exactly
 //     1.5·2^23 + acc, so no int->float conversion is needed.
 //   * PV as Oᵀ = Vᵀ·Pᵀ: the softmax output in the S layout is directly the B
-//     operand; V comes pre-packed (pre-pass) in A-operand order, so LDS reads
-//     are contiguous 16/32-byte lane vectors.  FP16: v_mfma_f32_32x32x16_f16.
-//     FP8: v_mfma_f32_32x32x64_f8f6f4 contracts exactly one 64-key tile.
-//   * K̂ and V tiles stream into a 3-stage LDS ring with buffer_load ... lds
+//     operand.  FP16: the input's V rows, read from LDS with the transposing
+//     ds_read_b64_tr_b16 into v_mfma_f32_32x32x16_f16's A operand.  FP8: V
+//     pre-packed (pre-pass) in A-operand order; v_mfma_f32_32x32x64_f8f6f4
+//     contracts exactly one 64-key tile.
+//   * K̂ and V tiles stream into a 4-stage LDS ring with buffer_load ... lds
 //     (no staging registers; out-of-range K̂ rows read as zero through the
 //     buffer descriptor's size).  Tile t+2 is requested while tile t is being
 //     consumed, so each tile has two iterations to arrive; one barrier per tile.
@@ -113,10 +114,13 @@ __device__ __forceinline__ int k_lds_chunk(int r, int c) {
 // lanes q, 4 + q, 8 + q, 12 + q address, in that order (probed on the
 // hardware).  So lane (g = l/16, j = (l/4)%4, q = l%4) addresses key row
 // 16kc + 8r + 4(g/2) + j (r = 0, 1: the two reads) at channels
-// 32dt + 16(g%2) + 4q .. +3.  The four rows a group reads share a bank line
-// (d = 128) or two (d = 64); XOR-ing the 16-byte chunk index with 2·(row % 4)
-// spreads the group's 16 chunks over 128 distinct bytes.
-__device__ __forceinline__ int v_lds_chunk16(int r, int c) { return c ^ (2 * (r & 3)); }
+// 32dt + 16(g%2) + 4q .. +3.  The hardware serves such a read 32 lanes at a
+// time: four rows, 64 bytes of each.  The tile therefore sits in LDS as D/32
+// column slabs [dt][key][32 channels] of 64-byte row segments, four segments
+// to a 256-byte bank line: the four rows of one half-read cover all 64 banks
+// once, and every fragment is the lane's one base plus a constant offset.
+constexpr int kVSeg = 64;             // bytes of one key's 32 channels
+constexpr int kVSlab = kKBlock * kVSeg;  // one 32-channel slab of a tile
 
 typedef short v4s16 __attribute__((__vector_size__(8)));
 typedef short v8s16 __attribute__((__vector_size__(16)));
@@ -130,28 +134,24 @@ __device__ __forceinline__ v8h v_frag_tr(const char* __restrict__ p, int row_byt
   return __builtin_bit_cast(v8h, (v8s16)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// This lane's two LDS byte offsets inside a V tile (even and odd 32-channel
-// steps): key row 4(g/2) + j, chunk (8·parity + 4(g%2) + q) ^ 4j in 8-byte units.
-template <int D>
-__device__ __forceinline__ void v_tr_bases(int lane, int& even, int& odd) {
+// This lane's LDS byte offset inside a V tile's slab: key row 4(g/2) + j,
+// channels 16(g%2) + 4q of the slab.
+__device__ __forceinline__ int v_tr_base(int lane) {
   const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
-  const int row = 4 * (g >> 1) + j;
-  even = row * 2 * D + (((4 * (g & 1) + q) ^ (4 * j)) * 8);
-  odd = row * 2 * D + (((8 + 4 * (g & 1) + q) ^ (4 * j)) * 8);
+  return (4 * (g >> 1) + j) * kVSeg + 32 * (g & 1) + 8 * q;
 }
 
 // Fragment (kc, dt): 16-key block kc, 32-channel step dt.
-template <int D>
-__device__ __forceinline__ v8h v_frag(const char* __restrict__ vstage, int even, int odd, int kc, int dt) {
-  return v_frag_tr(vstage + (dt & 1 ? odd : even) + 16 * kc * 2 * D + 16 * (dt >> 1) * 8, 2 * D);
+__device__ __forceinline__ v8h v_frag(const char* __restrict__ vstage, int base, int kc, int dt) {
+  return v_frag_tr(vstage + base + dt * kVSlab + 16 * kc * kVSeg, kVSeg);
 }
 
 // Request K̂ tile t (rows 64t..64t+63 of the head-sequence, zeros past its end)
 // and V tile t into one LDS stage.  kbase/kbytes bound the head-sequence's K̂
-// rows; vbase/vbytes its fp16 V rows (FP16 PV, stored with the V swizzle) or
+// rows; vbase/vbytes its fp16 V rows (FP16 PV, stored as 32-channel slabs) or
 // packed e4m3 tiles (FP8); reads past them return zero.
 // Lane i of a DMA instruction lands at the instruction's LDS base + 16·i, so
-// each lane fetches the global chunk that belongs at its swizzled position.
+// each lane fetches the global chunk that belongs at its LDS position.
 template <int D, bool FP8, int NT = kThreads, bool SM = false>
 __device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const void* vbase, int vbytes, int t,
                                            char* stage, int w, int lane, const SlotSrc& ss = SlotSrc{}) {
@@ -178,10 +178,10 @@ __device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const 
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + base * 16), 16,
                                                t * G::VBYTES + (base + lane) * 16, 0, 0, 0);
     } else {
-      constexpr int CPRV = D / 8;  // 16-byte chunks per fp16 row
+      // LDS chunk p: slab p/256, key (p/4)%64, 16-byte piece p%4 of its segment
       const int p = base + lane;
-      const int r = p / CPRV;
-      const unsigned off = (unsigned)(t * kKBlock + r) * (2u * D) + 16u * v_lds_chunk16(r, p % CPRV);
+      const int r = (p >> 2) & (kKBlock - 1);
+      const unsigned off = (unsigned)(t * kKBlock + r) * (2u * D) + (unsigned)((p >> 8) * kVSeg + 16 * (p & 3));
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + base * 16), 16, (int)off, 0, 0,
                                                0);
     }
@@ -381,13 +381,12 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ vstage, int lan
                                         const v8i& pk8, v16f (&O)[D / 32]) {
   constexpr int DT = D / 32;
   if (!FP8) {
-    int ve, vo;
-    v_tr_bases<D>(lane, ve, vo);
+    const int vb = v_tr_base(lane);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_frag<D>(vstage, ve, vo, kc, dt), pk16[kc], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_frag(vstage, vb, kc, dt), pk16[kc], O[dt], 0, 0, 0);
   } else {
     const v8i* lv = reinterpret_cast<const v8i*>(vstage);
 #pragma unroll
@@ -415,11 +414,10 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
   v4i kf[2][DT];
   load_k_frags<D>(reinterpret_cast<const v4i*>(kstage), kf, r32, gg);
   if (!FP8) {
-    int ve, vo;
-    v_tr_bases<D>(lane, ve, vo);
+    const int vb = v_tr_base(lane);
     v8h vf[4 * DT];
 #pragma unroll
-    for (int i = 0; i < 4 * DT; ++i) vf[i] = v_frag<D>(vstage, ve, vo, i / DT, i % DT);
+    for (int i = 0; i < 4 * DT; ++i) vf[i] = v_frag(vstage, vb, i / DT, i % DT);
     qk_half<D, SM>(kf, qf, S, lslots, gg);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
