@@ -189,3 +189,33 @@ def test_q_per_token_workload(name):
         ref1 = o1(views, x.v[b, h], rows, w.causal, w.pv_mode)
         ref2 = O.sdpa_fp64_rows(x.q[b, h], x.k[b, h], x.v[b, h], rows, w.causal)
         check_out(o[b, h, rows], ref1, ref2, f"q_per_token {name} b={b} h={h}")
+
+
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_q_per_token_large_magnitude(causal, d, pv_mode):
+    """Inputs ×30: per-lane factors δQ_i·δK·log2(e) well above 2^-7, so the
+    FP16 path's exact-log2 conversion decides lane by lane."""
+    say(f"case q_per_token large magnitude d={d} causal={causal} pv={pv_mode}")
+    B, H, n = 1, 2, 300
+    x = workloads.generate_custom(760 + d, B, H, n, d, k_bias=3.0, q_bias=1.0)
+    q = (x.q.astype(np.float32) * np.float32(30.0)).astype(np.float16)
+    k = (x.k.astype(np.float32) * np.float32(30.0)).astype(np.float16)
+    o = host(sage.sage_attn_fwd(dev(q), dev(k), dev(x.v), is_causal=causal, pv_mode=pv_mode, q_per_token=True))
+    quant = O.quant_qk_dense(q, k, q_per_token=True)
+    c2 = float(quant["q_scale"].max()) * float(quant["k_scale"].max()) * 1.4426950408889634
+    assert c2 > 2.0 ** -7, c2
+    rows = np.arange(n)
+    for h in range(H):
+        views = O.head_views_dense(quant, 0, h)
+        ref1 = o1(views, x.v[0, h], rows, causal, pv_mode)
+        ref2 = O.sdpa_fp64_rows(q[0, h], k[0, h], x.v[0, h], rows, causal)
+        ours = np.asarray(o[0, h], np.float64)
+        assert np.isfinite(ours).all()
+        err = np.abs(ours - ref1).max()
+        c1, c2o = cos(ours, ref1), cos(ours, ref2)
+        say(f"  h={h}: max_abs_vs_O1={err:.3e} cos_O1={c1:.6f} cos_O2={c2o:.6f}")
+        assert err <= MAX_ABS and c1 >= COS_O1, (h, err, c1)
+        # at this magnitude the method itself is further from exact attention
+        assert c2o >= min(COS_O2, cos(ref1, ref2) - 1e-4), (h, c2o)

@@ -370,3 +370,34 @@ def test_smooth_q_workload(name):
                                 None if vq is None else (vq[0][b, h], vq[1][b, h]))
         o2 = O.sdpa_fp64_rows(x.q[b, h], x.k[b, h], x.v[b, h], rows, w.causal)
         check_out(o[b, h, rows], o1, o2, f"smooth {name} b={b} h={h}", bnd)
+
+
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_smooth_q_large_magnitude(causal, d, pv_mode):
+    """Inputs ×30: large per-tile factors (the FP16 path's exact-log2
+    conversion) together with smoothing terms that may not fit the integer
+    accumulator (the fp32 fallback halves); every row against the method."""
+    say(f"case smooth_q large magnitude d={d} causal={causal} pv={pv_mode}")
+    B, H, n = 1, 2, 300
+    x = workloads.generate_custom(560 + d, B, H, n, d, k_bias=3.0, q_bias=3.0)
+    q = (x.q.astype(np.float32) * np.float32(30.0)).astype(np.float16)
+    k = (x.k.astype(np.float32) * np.float32(30.0)).astype(np.float16)
+    o = host(sage.sage_attn_fwd(dev(q), dev(k), dev(x.v), is_causal=causal, pv_mode=pv_mode, smooth_q=True))
+    quant = O.quant_qk_dense(q, k, smooth_q=True)
+    c2 = float(quant["q_scale"].max()) * float(quant["k_scale"].max()) * float(LOG2E)
+    assert c2 > 2.0 ** -7, c2
+    rows = np.arange(n)
+    for h in range(H):
+        ref1, _, _, bound = o1_rows(quant, k[0, h], x.v[0, h], 0, h, rows, causal, pv_mode)
+        ref2 = O.sdpa_fp64_rows(q[0, h], k[0, h], x.v[0, h], rows, causal)
+        ours = np.asarray(o[0, h], np.float64)
+        assert np.isfinite(ours).all()
+        diff = np.abs(ours - ref1)
+        c1, c2o = cos(ours, ref1), cos(ours, ref2)
+        say(f"  h={h}: max_abs_vs_O1={diff.max():.3e} (beyond open fp8 codes {(diff - bound).max():.3e}) "
+            f"cos_O1={c1:.6f} cos_O2={c2o:.6f}")
+        assert (diff - bound).max() <= MAX_ABS and c1 >= COS_O1, (h, diff.max(), c1)
+        # at this magnitude the method itself is further from exact attention
+        assert c2o >= min(COS_O2, cos(ref1, ref2) - 1e-4), (h, c2o)
