@@ -370,6 +370,43 @@ def test_large_magnitude_inputs(scale, pv_mode, d, causal):
         check_out(o[0, h], o1, o2, f"x{scale} {pv_mode} d={d} h={h}", min(COS_O2, cos(o1, o2) - 1e-4))
 
 
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_mixed_magnitudes(d, pv_mode):
+    """Sequences of ordinary and ×30 magnitude in one packed call: the
+    exact-log2 conversion is on for some waves and off for others."""
+    lens = [200, 130, 65, 300, 1, 257]
+    mags = [1.0, 30.0, 1.0, 8.0, 30.0, 30.0]
+    for causal in (False, True):
+        say(f"case varlen mixed magnitudes d={d} causal={causal} pv={pv_mode}")
+        x = workloads.generate_custom(330 + d, 0, 2, 0, d, k_bias=3.0, lengths=lens)
+        q = x.q.astype(np.float32)
+        k = x.k.astype(np.float32)
+        for i, m in enumerate(mags):
+            a, b = int(x.cu_seqlens[i]), int(x.cu_seqlens[i + 1])
+            q[:, a:b] *= np.float32(m)
+            k[:, a:b] *= np.float32(m)
+        q, k = q.astype(np.float16), k.astype(np.float16)
+        cu = dev(x.cu_seqlens)
+        o = host(sage.sage_attn_varlen_fwd(dev(q), dev(k), dev(x.v), cu, max(lens), is_causal=causal,
+                                           pv_mode=pv_mode))
+        quant = O.quant_qk_varlen(q, k, x.cu_seqlens)
+        for i, n in enumerate(lens):
+            a = int(x.cu_seqlens[i])
+            for h in range(2):
+                qi, qs, ki, ks = O.head_views_varlen(quant, x.cu_seqlens, i, h)
+                vv = x.v[h, a:a + n]
+                rows = np.arange(n)
+                if pv_mode == "fp8":
+                    vc, vs = O.quant_v_fp8(vv)
+                    o1 = O.sage_attention_rows(qi, qs, ki, ks, vc, rows, causal, "fp8", vs)
+                else:
+                    o1 = O.sage_attention_rows(qi, qs, ki, ks, vv, rows, causal, "fp16")
+                o2 = O.sdpa_fp64_rows(q[h, a:a + n], k[h, a:a + n], vv, rows, causal)
+                check_out(o[h, a:a + n], o1, o2, f"x{mags[i]} seq={i} n={n} h={h}",
+                          min(COS_O2, cos(o1, o2) - 1e-4))
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads: whole-tensor bit-exact quantisation, sampled output rows
 # ---------------------------------------------------------------------------
