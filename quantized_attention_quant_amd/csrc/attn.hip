@@ -146,6 +146,16 @@ __device__ __forceinline__ v8h v_frag(const char* __restrict__ vstage, int base,
   return v_frag_tr(vstage + base + dt * kVSlab + 16 * kc * kVSeg, kVSeg);
 }
 
+// FP8 PV: the pre-pass packs each d tile's A operands as 64 lanes x 32 bytes.
+// In LDS the two 16-byte halves sit apart (bytes 0-15 of every lane, then
+// bytes 16-31), so each 128-bit read covers 64 consecutive chunks: with the
+// lanes 32 bytes apart, lanes i and i+8 of a 16-lane group would share banks.
+__device__ __forceinline__ v8i v_frag_fp8(const char* __restrict__ vstage, int lane, int dt) {
+  const v4i* p = reinterpret_cast<const v4i*>(vstage) + dt * 128 + lane;
+  const v4i lo = p[0], hi = p[64];
+  return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+}
+
 // Request K̂ tile t (rows 64t..64t+63 of the head-sequence, zeros past its end)
 // and V tile t into one LDS stage.  kbase/kbytes bound the head-sequence's K̂
 // rows; vbase/vbytes its fp16 V rows (FP16 PV, stored as 32-channel slabs) or
@@ -175,8 +185,11 @@ __device__ __forceinline__ void issue_tile(const void* kbase, int kbytes, const 
   for (int j = 0; j < G::VI; ++j) {
     const int base = (w * G::VI + j) * 64;
     if (FP8) {
+      // LDS chunk p: d tile p/128, half (p/64)%2 of lane p%64's operand
+      const int p = base + lane;
+      const int src = (p & ~127) + 2 * (p & 63) + ((p >> 6) & 1);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_ptr_t)(stage + G::KBYTES + base * 16), 16,
-                                               t * G::VBYTES + (base + lane) * 16, 0, 0, 0);
+                                               t * G::VBYTES + src * 16, 0, 0, 0);
     } else {
       // LDS chunk p: slab p/256, key (p/4)%64, 16-byte piece p%4 of its segment
       const int p = base + lane;
@@ -388,10 +401,10 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ vstage, int lan
       for (int dt = 0; dt < DT; ++dt)
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_frag(vstage, vb, kc, dt), pk16[kc], O[dt], 0, 0, 0);
   } else {
-    const v8i* lv = reinterpret_cast<const v8i*>(vstage);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(lv[dt * 64 + lane], pk8, O[dt], 0, 0, 0, 0, 0, 0);
+      O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(v_frag_fp8(vstage, lane, dt), pk8, O[dt], 0, 0, 0, 0,
+                                                              0, 0);
   }
 }
 
@@ -425,10 +438,9 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
       for (int dt = 0; dt < DT; ++dt)
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[kc * DT + dt], pk16[kc], O[dt], 0, 0, 0);
   } else {
-    const v8i* lv = reinterpret_cast<const v8i*>(vstage);
     v8i vf[DT];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vf[dt] = lv[dt * 64 + lane];
+    for (int dt = 0; dt < DT; ++dt) vf[dt] = v_frag_fp8(vstage, lane, dt);
     qk_half<D, SM>(kf, qf, S, lslots, gg);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
