@@ -43,6 +43,14 @@ constexpr int kMagicBias = 0x4B400000;  // fp32 bits of 1.5 * 2^23
 constexpr float kLog2eF = 1.4426950408889634f;
 constexpr int kQbBlocksPerGroup = 32;   // Q blocks per MFMA column group
 
+// LDS layout of a group's B operand, in 16-byte chunks: run (kstep, hi/lo) at
+// kBRun·(2·kstep + hi/lo), the lanes of column half cg at kBHalf·cg + block.
+// The 16 lanes of one write (8 channel parts x 2 blocks) then land on 16
+// distinct bank groups at d = 64 and d = 128 (a stride of 64 chunks put them
+// all on one), and each read stays 16 consecutive chunks per 16 lanes.
+constexpr int kBRun = 73;
+constexpr int kBHalf = 40;
+
 template <int D>
 constexpr int kSlotLimit = (1 << 22) - 1 - 127 * 127 * D;
 
@@ -100,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void q_bias_kernel(QBiasArgs a) {
   const bool wave_live = kKBlock * t < n;
 
   __shared__ float km_s[D];
-  __shared__ v8h bfrag[KS * 2 * 64];  // B operand of one group: (kstep, hi/lo, lane)
+  __shared__ v8h bfrag[KS * 2 * kBRun];  // B operand of one group: (kstep, hi/lo, lane)
   __shared__ int eq_s[kQbBlocksPerGroup];
   if (tid < D) km_s[tid] = a.k_mean[hsk * D + tid];
   __syncthreads();
@@ -184,8 +192,8 @@ __global__ __launch_bounds__(kThreads) void q_bias_kernel(QBiasArgs a) {
         const int c = CPT * part + 8 * m;
         const int kk = c / 16, cg = (c % 16) / 8;
         const v8h hi = split_hi(x);
-        bfrag[(2 * kk) * 64 + 32 * cg + bl] = hi;
-        bfrag[(2 * kk + 1) * 64 + 32 * cg + bl] = split_lo(x, hi);
+        bfrag[(2 * kk) * kBRun + kBHalf * cg + bl] = hi;
+        bfrag[(2 * kk + 1) * kBRun + kBHalf * cg + bl] = split_lo(x, hi);
       }
     }
     __syncthreads();
@@ -195,7 +203,8 @@ __global__ __launch_bounds__(kThreads) void q_bias_kernel(QBiasArgs a) {
       for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        const v8h bhi = bfrag[(2 * kk) * 64 + lane], blo = bfrag[(2 * kk + 1) * 64 + lane];
+        const int bl = kBHalf * gg + r32;
+        const v8h bhi = bfrag[(2 * kk) * kBRun + bl], blo = bfrag[(2 * kk + 1) * kBRun + bl];
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[kk], bhi, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[kk], blo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[kk], bhi, acc, 0, 0, 0);
