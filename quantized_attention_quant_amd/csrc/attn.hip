@@ -591,9 +591,10 @@ void attn_fwd_kernel(AttnArgs a) {
   const int nqb = ceil_div(g.N, kQBlock);
   const int nkb = ceil_div(g.N, kKBlock);
   const int nwb = ceil_div(g.N, kAttnRows);
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int wb = nwb - 1 - logical % nwb;  // heavy (late) causal blocks first
-  const int hb = logical / nwb;
+  // causal: pair head-sequences when two of them (K̂ + V per key) fit one L2
+  const bool pair = CAUSAL && 2 * (int64_t)g.N * (D + G::VBYTES / kKBlock) <= kXcdL2Bytes;
+  int wb, hb;
+  work_item(xcd_remap(blockIdx.x, gridDim.x), nwb, g.H * g.B, pair, wb, hb);
   const int h = hb / g.B, b = hb % g.B;
   int64_t row0;
   int n;
@@ -1038,9 +1039,10 @@ void attn_mx_kernel(MxArgs a) {
 
   const SeqGeom& g = a.g;
   const int nwb = ceil_div(g.N, kAttnRows);
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int wb = nwb - 1 - logical % nwb;
-  const int hb = logical / nwb;
+  // causal: pair head-sequences when two of them (codes and scales per key) fit one L2
+  const bool pair = CAUSAL && 2 * (int64_t)g.N * ((G::KBYTES + G::VBYTES + kMxAuxBytes) / kKBlock) <= kXcdL2Bytes;
+  int wb, hb;
+  work_item(xcd_remap(blockIdx.x, gridDim.x), nwb, g.H * g.B, pair, wb, hb);
   const int h = hb / g.B, b = hb % g.B;
   int64_t row0;
   int n;

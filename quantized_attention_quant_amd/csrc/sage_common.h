@@ -76,6 +76,34 @@ __device__ __forceinline__ int xcd_remap(int bid, int total) {
   return x * q + (x < r ? x : r) + local;
 }
 
+// Query block wb (of nwb) and head-sequence hb (of nhb) of a logical work
+// index.  By default the blocks of one head-sequence are consecutive,
+// heaviest (last) first, so an XCD streams one head-sequence's K/V through
+// its L2 at a time.  With `pair` (causal, where block wb costs wb + 1 units)
+// the blocks of head-sequences 2p and 2p + 1 alternate, heaviest first: that
+// evens out the end of each XCD's run (in a greedy-dispatch model at
+// 4x32x4096, 16 % over the balanced time one head-sequence at a time, 6 % in
+// pairs), at the price of two head-sequences' K/V in L2 at once, so callers
+// pair only when both fit.  A bijection on [0, nwb·nhb).
+__device__ __forceinline__ void work_item(int logical, int nwb, int nhb, bool pair, int& wb, int& hb) {
+  if (!pair) {
+    wb = nwb - 1 - logical % nwb;
+    hb = logical / nwb;
+    return;
+  }
+  const int p = logical / (2 * nwb), i = logical % (2 * nwb);
+  if (2 * p + 1 < nhb) {
+    wb = nwb - 1 - i / 2;
+    hb = 2 * p + (i & 1);
+  } else {  // the last head-sequence of an odd count
+    wb = nwb - 1 - i;
+    hb = 2 * p;
+  }
+}
+
+// One XCD's L2 (MI355X: 4 MB): the bound for pairing head-sequences.
+constexpr int64_t kXcdL2Bytes = int64_t(4) << 20;
+
 // MXFP4 block exponent (OCP microscaling, E8M0 range): the smallest X with
 // amax <= 6·2^X, 6 being e2m1's largest value.  With amax = f·2^e,
 // f in [0.5, 1): X = e - 3 + (f > 0.75); clamped to [-127, 127]; amax = 0
