@@ -287,10 +287,19 @@ __device__ __forceinline__ void load_k_frags(const v4i* __restrict__ lds_k, v4i 
 // key (lslots: the wave's Q block's 64 values in LDS) + Σ q̂·k̂.
 template <int D, bool SM = false>
 __device__ __forceinline__ void qk_half(const v4i (&kf)[2][D / 32], const v4i (&qf)[D / 32], v16i (&S)[2],
-                                        const v4i* __restrict__ lslots = nullptr, int g = 0) {
+                                        const v4i* __restrict__ lslots = nullptr, int g = 0,
+                                        const v16i* magic = nullptr) {
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     v16i acc;
+    if (!SM && magic) {
+      // the first MFMA reads the start value from the persistent registers
+      acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[s][0], qf[0], *magic, 0, 0, 0);
+#pragma unroll
+      for (int ks = 1; ks < D / 32; ++ks) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[s][ks], qf[ks], acc, 0, 0, 0);
+      S[s] = acc;
+      continue;
+    }
     if (SM) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -417,7 +426,8 @@ template <int D, bool FP8, bool SM = false>
 __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, const char* __restrict__ vstage,
                                             int lane, int r32, int gg, const v4i (&qf)[D / 32], v16i (&S)[2],
                                             const v8h (&pk16)[4], const v8i& pk8, v16f (&O)[D / 32],
-                                            const v4i* __restrict__ lslots = nullptr) {
+                                            const v4i* __restrict__ lslots = nullptr,
+                                            const v16i* magic = nullptr) {
   constexpr int DT = D / 32;
   constexpr int NK = 2 * DT + (SM ? 8 : 0);  // K̂ fragment (+ initial value) reads (128-bit)
   constexpr int NV = FP8 ? 2 * DT : 8 * DT;  // V fragment reads (FP8: 128-bit; FP16: 64-bit transposing)
@@ -431,7 +441,7 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
     v8h vf[4 * DT];
 #pragma unroll
     for (int i = 0; i < 4 * DT; ++i) vf[i] = v_frag(vstage, vb, i / DT, i % DT);
-    qk_half<D, SM>(kf, qf, S, lslots, gg);
+    qk_half<D, SM>(kf, qf, S, lslots, gg, magic);
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc)
 #pragma unroll
@@ -441,7 +451,7 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
     v8i vf[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[dt] = v_frag_fp8(vstage, lane, dt);
-    qk_half<D, SM>(kf, qf, S, lslots, gg);
+    qk_half<D, SM>(kf, qf, S, lslots, gg, magic);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       O[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[dt], pk8, O[dt], 0, 0, 0, 0, 0, 0);
@@ -638,6 +648,19 @@ void attn_fwd_kernel(AttnArgs a) {
                        npad};
 
   WaveCtx<D, FP8> c;
+  // FP16 PV at d=128: the accumulator start value 1.5·2^23 kept in 16
+  // registers for the whole loop (the first QKᵀ MFMA of each half reads it),
+  // in place of 16 vector moves per tile; opaque to the compiler so that it is
+  // not re-materialised.  Measured -0.8 % at 16K, -1.8 % at 16K causal, but
+  // +2.6 % for the FP8 PV kernel, which keeps the moves; d=64 has no registers
+  // to spare at four waves per SIMD.
+  v16i mg;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int m = kMagicI;
+    if (D == 128 && !FP8) asm volatile("" : "+v"(m));
+    mg[i] = m;
+  }
   load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
   // δQ: the wave's block scale (uniform), or this lane's query's own scale
   const float dq = QM == kQmToken ? (qrow < n ? a.q_scale[row0 + qrow] : 0.f)
@@ -758,7 +781,8 @@ void attn_fwd_kernel(AttnArgs a) {
                               c.qf, c.S, c.pk16, c.pk8, c.O,
                               reinterpret_cast<const v4i*>(smem + (t % kRingStages) * G::STAGE + G::KBYTES +
                                                            G::VBYTES) +
-                                  32 * (wqb - q0 / kQBlock));
+                                  32 * (wqb - q0 / kQBlock),
+                              (D == 128 && !FP8) ? &mg : nullptr);
     if (lead) softmax_step(t);
     // tile t+1 landed before anyone's next matrix phase (later tiles may fly)
     if (lead) wait_tiles<L>(max(0, min(kAhead - 1, ntiles - 2 - t)));
