@@ -281,6 +281,25 @@ __device__ __forceinline__ void load_k_frags(const v4i* __restrict__ lds_k, v4i 
     for (int ks = 0; ks < D / 32; ++ks) kf[s][ks] = lds_k[k_lds_chunk<D>(32 * s + r32, 2 * ks + g)];
 }
 
+// This lane's byte offsets of its K̂ fragments inside a K̂ tile (row r32, chunk
+// column 2ks + g); rows 32..63 sit 32·D bytes further (the swizzle key of
+// row r + 32 equals that of row r).  Computed once, so a fragment address is
+// one add of the tile's stage offset.
+template <int D>
+__device__ __forceinline__ void k_frag_offsets(int r32, int g, int (&ofs)[D / 32]) {
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) ofs[ks] = 16 * k_lds_chunk<D>(r32, 2 * ks + g);
+}
+template <int D>
+__device__ __forceinline__ void load_k_frags_at(const char* __restrict__ kstage, const int (&ofs)[D / 32],
+                                                v4i (&kf)[2][D / 32]) {
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+      kf[s][ks] = *reinterpret_cast<const v4i*>(kstage + ofs[ks] + s * 32 * D);
+}
+
 // Sᵀ of one 32-query half for one 64-key tile: S[s] covers keys 32s..32s+31;
 // lane (r32, g) reg i holds key 32s + 8(i/4) + 4g + i%4 of query r32, as
 // magic + Σ q̂·k̂ — or, with a smoothed Q (SM), as the initial value of that
@@ -423,8 +442,9 @@ __device__ __forceinline__ void pv_tile(const char* __restrict__ vstage, int lan
 // transposing reads for FP16) while any remain, so each LDS read has several
 // MFMAs (>= 256 cycles) to land before its use.
 template <int D, bool FP8, bool SM = false>
-__device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, const char* __restrict__ vstage,
-                                            int lane, int r32, int gg, const v4i (&qf)[D / 32], v16i (&S)[2],
+__device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, const int (&kofs)[D / 32],
+                                            const char* __restrict__ vstage, int lane, int gg,
+                                            const v4i (&qf)[D / 32], v16i (&S)[2],
                                             const v8h (&pk16)[4], const v8i& pk8, v16f (&O)[D / 32],
                                             const v4i* __restrict__ lslots = nullptr,
                                             const v16i* magic = nullptr) {
@@ -435,7 +455,7 @@ __device__ __forceinline__ void matrix_both(const char* __restrict__ kstage, con
   constexpr int NQK = 2 * DT;                // QKᵀ MFMAs
   constexpr int NPV = FP8 ? DT : 4 * DT;     // PV MFMAs
   v4i kf[2][DT];
-  load_k_frags<D>(reinterpret_cast<const v4i*>(kstage), kf, r32, gg);
+  load_k_frags_at<D>(kstage, kofs, kf);
   if (!FP8) {
     const int vb = v_tr_base(lane);
     v8h vf[4 * DT];
@@ -648,6 +668,8 @@ void attn_fwd_kernel(AttnArgs a) {
                        npad};
 
   WaveCtx<D, FP8> c;
+  int kofs[DT];
+  k_frag_offsets<D>(r32, gg, kofs);
   // FP16 PV at d=128: the accumulator start value 1.5·2^23 kept in 16
   // registers for the whole loop (the first QKᵀ MFMA of each half reads it),
   // in place of 16 vector moves per tile; opaque to the compiler so that it is
@@ -775,14 +797,16 @@ void attn_fwd_kernel(AttnArgs a) {
     // One place for both MFMA parts keeps O and S in fixed registers.  At t = 0
     // the pending P is zero (O += 0·V of tile 0, which has landed); at t = nact
     // the QKᵀ result is not used.
-    if (t <= nact && nact > 0)
-      matrix_both<D, FP8, SM>(smem + (t % kRingStages) * G::STAGE,
-                              smem + ((t == 0 ? 0 : t - 1) % kRingStages) * G::STAGE + G::KBYTES, lane, r32, gg,
-                              c.qf, c.S, c.pk16, c.pk8, c.O,
-                              reinterpret_cast<const v4i*>(smem + (t % kRingStages) * G::STAGE + G::KBYTES +
-                                                           G::VBYTES) +
+    if (t <= nact && nact > 0) {
+      // stage offsets are wave-uniform: scalar arithmetic, one vector add per address
+      const int kst = __builtin_amdgcn_readfirstlane((t % kRingStages) * G::STAGE);
+      static_assert((kRingStages & (kRingStages - 1)) == 0, "ring index by mask");
+      const int vst = (t > 0 ? (t - 1) & (kRingStages - 1) : 0) * G::STAGE;
+      matrix_both<D, FP8, SM>(smem + kst, kofs, smem + vst + G::KBYTES, lane, gg, c.qf, c.S, c.pk16, c.pk8, c.O,
+                              reinterpret_cast<const v4i*>(smem + kst + G::KBYTES + G::VBYTES) +
                                   32 * (wqb - q0 / kQBlock),
                               (D == 128 && !FP8) ? &mg : nullptr);
+    }
     if (lead) softmax_step(t);
     // tile t+1 landed before anyone's next matrix phase (later tiles may fly)
     if (lead) wait_tiles<L>(max(0, min(kAhead - 1, ntiles - 2 - t)));
