@@ -409,7 +409,9 @@ __device__ __forceinline__ float exp_pack_fp8(const float (&F)[2][16], float mx,
       p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(F[s][i0 + j] - mx, c2, cterm));
       lsum += p[j];
     }
-    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+    // the two conversions write the low and then the high half of the word:
+    // starting from the old (dead) value saves clearing a register first
+    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pk[q], false);
     pk[q] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
   }
   return lsum;
@@ -1069,7 +1071,9 @@ __device__ __forceinline__ void mx_softmax(MxWave<D>& c, float c2) {
   for (int q = 0; q < 4; ++q) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) part[q] += p[q][j];
-    w[q] = mx_pack8(p[q], sc);
+    // d=128: start from the previous P, dead here (at d=64 keeping it live
+    // that long costs a spill)
+    w[q] = mx_pack8(p[q], sc, D == 128 ? c.pk[q] : 0);
   }
   const float lsum = (part[0] + part[1]) + (part[2] + part[3]);
   c.pk = v4i{(int)w[0], (int)w[1], (int)w[2], (int)w[3]};

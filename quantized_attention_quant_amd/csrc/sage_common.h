@@ -117,8 +117,10 @@ __device__ __forceinline__ int mx_exponent(float amax) {
 
 // Eight values as e2m1 nibbles of fp4(x / scale) (value j at bits 4j; round to
 // nearest even, saturating at ±6 — the hardware conversion).
-__device__ __forceinline__ uint32_t mx_pack8(const float (&x)[8], float scale) {
-  int w = 0;
+// The four conversions fill all four bytes, so `init` (any value, e.g. a dead
+// register) only spares clearing one first.
+__device__ __forceinline__ uint32_t mx_pack8(const float (&x)[8], float scale, int init = 0) {
+  int w = init;
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[0], x[1], scale, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[2], x[3], scale, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, x[4], x[5], scale, 2);
