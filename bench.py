@@ -308,10 +308,10 @@ def main():
         # the fused attention kernel alone, re-run on the workspace the last step filled
         reps = max(args.steps, 5)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, **opts)
+        sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, q=q, **opts)
         e0.record(stream)
         for _ in range(reps):
-            sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, **opts)
+            sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, q=q, **opts)
         e1.record(stream)
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / reps

@@ -57,7 +57,7 @@ SIGNATURES = {
     "sage_test_workspace_layout": (_c.c_int, [_c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int64,
                                               _c.c_int, _c.c_int, _c.c_int, _c.POINTER(_c.c_size_t)]),
     "sage_test_qk_tiles": (_c.c_int, [_P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P, _c.c_int, _P, _P]),
-    "sage_test_attn_from_workspace": (_c.c_int, [_P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+    "sage_test_attn_from_workspace": (_c.c_int, [_P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                                  _c.c_int, _c.c_int, _c.c_int, _P, _c.c_size_t, _P]),
 }
 
@@ -305,15 +305,19 @@ def sage_test_qk_tiles(q_int8: torch.Tensor, k_int8: torch.Tensor, tile_list: to
 def sage_test_attn_from_workspace(out: torch.Tensor, workspace: torch.Tensor, v: Optional[torch.Tensor] = None,
                                   is_causal: bool = False, pv_mode: str = "fp16", stream=None,
                                   H_kv: Optional[int] = None, smooth_q: bool = False,
-                                  q_per_token: bool = False) -> torch.Tensor:
+                                  q_per_token: bool = False, q: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Run only the fused attention kernel on a workspace filled by sage_attn_fwd
     (same shapes and options; v: that call's fp16 V, read directly in fp16 PV
-    mode); out fp16 [B,H,N,d] is written and returned."""
+    mode; q: that call's fp16 Q, which the kernel quantises itself without
+    options in fp16/fp8 PV mode); out fp16 [B,H,N,d] is written and returned."""
     _need(out, "out", torch.float16, 4)
     if v is not None:
         _need(v, "v", torch.float16, 4)
+    if q is not None:
+        _need(q, "q", torch.float16, 4)
     B, H, N, d = out.shape
-    st = lib().sage_test_attn_from_workspace(out.data_ptr(), 0 if v is None else v.data_ptr(), B, H,
+    st = lib().sage_test_attn_from_workspace(out.data_ptr(), 0 if q is None else q.data_ptr(),
+                                             0 if v is None else v.data_ptr(), B, H,
                                              H if H_kv is None else H_kv, N, d,
                                              int(bool(is_causal)), PV_MODES[pv_mode], _options(smooth_q, q_per_token),
                                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),

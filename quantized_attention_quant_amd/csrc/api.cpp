@@ -220,7 +220,12 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   float* fix = reinterpret_cast<float*>(ws + L.off[10]);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.off[11]);
 
-  sage::launch_quant_qk(g, gk, q, k, sm, q8, k8, qs, ks, km, qm, qtok, colsum, st);
+  // per-block Q without smoothing: the attention kernel quantises the fp16 Q
+  // itself (the same quantiser), so the pre-pass neither writes nor the
+  // kernel reads Q̂ and δQ
+  const bool qfuse = !sq && !qtok;
+  sage::launch_quant_qk(g, gk, q, k, sm, qfuse ? nullptr : q8, k8, qfuse ? nullptr : qs, ks, km, qm, qtok, colsum,
+                        st);
   int32_t* any = sq ? row_summaries(ws + L.off[11], g.B, g.H, g.N) : nullptr;
   if (sq) {
     sage::launch_zero(any, align16(sizeof(int32_t) * (size_t)g.B * g.H * ceil_div64(g.N, sage::kQBlock)), st);
@@ -236,6 +241,10 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   sage::AttnArgs a{q8, k8, qs, ks, fp8 ? vp : static_cast<const uint8_t*>(v), vs, static_cast<uint16_t*>(o), lse, g,
                    g.H / Hkv};
   a.q_per_token = qtok;
+  if (qfuse) {
+    a.q16 = static_cast<const uint16_t*>(q);
+    a.sm_scale = sm;
+  }
   if (sq) {
     a.qb_slots = slots;
     a.qb_fix = fix;
@@ -387,7 +396,8 @@ sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int
   return SAGE_OK;
 }
 
-sage_status_t sage_test_attn_from_workspace(void* o, const void* v, int B, int H, int H_kv, int N, int d,
+sage_status_t sage_test_attn_from_workspace(void* o, const void* q, const void* v, int B, int H, int H_kv, int N,
+                                            int d,
                                             int is_causal, sage_pv_mode_t pv_mode, int options,
                                             const void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   const sage_status_t s = check_dims(B, H, N, d);
@@ -399,6 +409,10 @@ sage_status_t sage_test_attn_from_workspace(void* o, const void* v, int B, int H
   if (pv_mode == SAGE_PV_FP16 && (!v || !aligned16(v))) return SAGE_ERR_INVALID_ARGUMENT;
   if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
+  // per-block Q without smoothing: the attention kernel quantises q itself, or,
+  // with q NULL, reads Q̂ and δQ from regions [0] and [2]
+  const bool qfuse = pv_mode != SAGE_MXFP4 && options == 0 && q != nullptr;
+  if (qfuse && !aligned16(q)) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
   const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, pv_mode, options);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
@@ -424,6 +438,10 @@ sage_status_t sage_test_attn_from_workspace(void* o, const void* v, int B, int H
                    fp8 ? reinterpret_cast<const uint8_t*>(ws + L.off[5]) : static_cast<const uint8_t*>(v),
                    reinterpret_cast<const float*>(ws + L.off[6]), static_cast<uint16_t*>(o), nullptr, g, H / H_kv};
   a.q_per_token = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
+  if (qfuse) {
+    a.q16 = static_cast<const uint16_t*>(q);
+    resolve_sm_scale(0.f, d, &a.sm_scale);
+  }
   if (options & SAGE_OPT_SMOOTH_Q) {
     a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[9]);
     a.qb_fix = reinterpret_cast<const float*>(ws + L.off[10]);

@@ -685,10 +685,42 @@ void attn_fwd_kernel(AttnArgs a) {
     if (D == 128 && !FP8) asm volatile("" : "+v"(m));
     mg[i] = m;
   }
-  load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
-  // δQ: the wave's block scale (uniform), or this lane's query's own scale
-  const float dq = QM == kQmToken ? (qrow < n ? a.q_scale[row0 + qrow] : 0.f)
-                                  : load_uniform(a.q_scale, hs * nqb + wqb_in);
+  // Per-block Q quantised here (q16 set): the lane's 16-channel runs of its
+  // query in fp32, the wave's largest |x| to LDS; the block's four waves'
+  // maxima are combined after the barrier below.  The codes and scale are
+  // those of the Q pre-pass (the same quantiser, in the same precision).
+  const bool qfuse = QM == kQmBlock && a.q16 != nullptr;
+  __shared__ float qmax_s[kAttnWaves];
+  float qx[DT][16];
+  float dq = 0.f;
+  if (qfuse) {
+    float amax = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < DT; ++ks) {
+      v4i raw[2] = {v4i{0, 0, 0, 0}, v4i{0, 0, 0, 0}};
+      if (qrow < n) {
+        const v4i* src = reinterpret_cast<const v4i*>(a.q16 + (row0 + qrow) * D + 32 * ks + 16 * gg);
+        raw[0] = src[0];
+        raw[1] = src[1];
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t wd = (uint32_t)raw[h2][j];
+          qx[ks][8 * h2 + 2 * j] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd & 0xffffu));
+          qx[ks][8 * h2 + 2 * j + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(wd >> 16));
+        }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(qx[ks][j]));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) qmax_s[w] = amax;
+  } else {
+    load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
+    // δQ: the wave's block scale (uniform), or this lane's query's own scale
+    dq = QM == kQmToken ? (qrow < n ? a.q_scale[row0 + qrow] : 0.f) : load_uniform(a.q_scale, hs * nqb + wqb_in);
+  }
   const float* __restrict__ ksc = a.k_scale + hsk * nkb;
   // smoothed Q: whether any half tile of this wave's Q block falls back (rare);
   // only then are the per-tile flags read
@@ -724,6 +756,26 @@ void attn_fwd_kernel(AttnArgs a) {
   // here also lets the compiler see that no later MFMA waits on the Q̂ loads
   wait_dma<0>();
   barrier_only();
+  if (qfuse) {
+    // the Q block of this wave: waves 4·(w/4) .. +3
+    const int wb0 = w & ~3;
+    const float amax =
+        __builtin_fmaxf(__builtin_fmaxf(qmax_s[wb0], qmax_s[wb0 + 1]), __builtin_fmaxf(qmax_s[wb0 + 2], qmax_s[wb0 + 3]));
+    const float s = amax / kInt8Max;
+    const float r = 1.0f / s;
+#pragma unroll
+    for (int ks = 0; ks < DT; ++ks) {
+      uint32_t wv[4] = {0u, 0u, 0u, 0u};  // an all-zero block (s = 0) has all codes 0
+      if (s > 0.f) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          wv[q4] = pack4_i8(int8_code(qx[ks][4 * q4], s, r), int8_code(qx[ks][4 * q4 + 1], s, r),
+                            int8_code(qx[ks][4 * q4 + 2], s, r), int8_code(qx[ks][4 * q4 + 3], s, r));
+      }
+      c.qf[ks] = v4i{(int)wv[0], (int)wv[1], (int)wv[2], (int)wv[3]};
+    }
+    dq = s * a.sm_scale;
+  }
   // FP16: can a tile's factor δQ·δK·log2(e) exceed kExactC2 in this wave?
   // Only then are its tiles checked one by one (rare inputs).
   const bool exact_wave = !FP8 && __any(dq * wave_max(dkmax) * kLog2e > kExactC2);

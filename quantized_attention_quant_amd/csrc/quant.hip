@@ -82,27 +82,6 @@ __device__ __forceinline__ float block_max256(float v) {
   return r;
 }
 
-// Symmetric INT8 code of x for a block scale s > 0: rint of the IEEE fp32
-// quotient fl32(x/s), clamped to ±127.  The quotient is first formed as
-// y = fl32(x·r) with r = fl32(1/s): since |x/s| <= 127·(1 + 2^-23), y lies
-// within 2.3e-5 of fl32(x/s), so rint(y) is the same integer unless y is within
-// that distance of a half-integer; only then is the exact quotient divided out.
-constexpr float kTieGuard = 6.103515625e-05f;  // 2^-14 > 2.3e-5
-
-__device__ __attribute__((noinline)) float exact_code(float x, float s) { return __builtin_rintf(x / s); }
-
-__device__ __forceinline__ int int8_code(float x, float s, float r) {
-  const float y = x * r;
-  float c = __builtin_rintf(y);
-  if (__builtin_expect(__builtin_fabsf(__builtin_fabsf(y - c) - 0.5f) <= kTieGuard, 0)) c = exact_code(x, s);
-  return (int)__builtin_amdgcn_fmed3f(c, -kInt8Max, kInt8Max);
-}
-
-__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
-  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
-         ((uint32_t)(d & 0xff) << 24);
-}
-
 // ---------------------------------------------------------------------------
 // Per-block INT8 of one block of ROWS tokens x D channels of fp32 values
 // x = fp16 input - shift.  MODE selects the shift:
@@ -627,7 +606,8 @@ void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const 
                      float* q_mean, bool q_per_token, long long* colsum, hipStream_t st) {
   // gq: Q's geometry (H query heads); gk: K's (its own head count), same
   // sequences.  q_mean != nullptr selects Q smoothing, q_per_token per-token
-  // Q scales (not both).
+  // Q scales (not both); with neither, q_int8 == nullptr leaves Q to the
+  // attention kernel (it quantises the fp16 Q itself).
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
   const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
   launch_zero(colsum, sizeof(long long) * (size_t)gk.B * gk.H * gk.d, st);
@@ -643,7 +623,7 @@ void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const 
     else if (q_per_token)                                                                                      \
       hipLaunchKernelGGL((quant_row_kernel<DD, kRowsPerBlock>), hs_grid(gq, kRowsPerBlock), blk, 0, st, q16,   \
                          gq, sm_scale, q_int8, q_scale);                                                       \
-    else                                                                                                       \
+    else if (q_int8)                                                                                           \
       hipLaunchKernelGGL((quant_block_kernel<DD, kQBlock, kShiftNone>), gqb, blk, 0, st, q16, gq,              \
                          (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);               \
     hipLaunchKernelGGL((quant_block_kernel<DD, kKBlock, kShiftKMean>), gkb, blk, 0, st, k16, gk, cs, 1.0f,     \

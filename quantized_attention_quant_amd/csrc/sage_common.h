@@ -104,6 +104,27 @@ __device__ __forceinline__ void work_item(int logical, int nwb, int nhb, bool pa
 // One XCD's L2 (MI355X: 4 MB): the bound for pairing head-sequences.
 constexpr int64_t kXcdL2Bytes = int64_t(4) << 20;
 
+// Symmetric INT8 code of x for a block scale s > 0: rint of the IEEE fp32
+// quotient fl32(x/s), clamped to ±127.  The quotient is first formed as
+// y = fl32(x·r) with r = fl32(1/s): since |x/s| <= 127·(1 + 2^-23), y lies
+// within 2.3e-5 of fl32(x/s), so rint(y) is the same integer unless y is within
+// that distance of a half-integer; only then is the exact quotient divided out.
+constexpr float kTieGuard = 6.103515625e-05f;  // 2^-14 > 2.3e-5
+
+static __device__ __attribute__((noinline)) float exact_code(float x, float s) { return __builtin_rintf(x / s); }
+
+__device__ __forceinline__ int int8_code(float x, float s, float r) {
+  const float y = x * r;
+  float c = __builtin_rintf(y);
+  if (__builtin_expect(__builtin_fabsf(__builtin_fabsf(y - c) - 0.5f) <= kTieGuard, 0)) c = exact_code(x, s);
+  return (int)__builtin_amdgcn_fmed3f(c, -kInt8Max, kInt8Max);
+}
+
+__device__ __forceinline__ uint32_t pack4_i8(int a, int b, int c, int d) {
+  return (uint32_t)(a & 0xff) | ((uint32_t)(b & 0xff) << 8) | ((uint32_t)(c & 0xff) << 16) |
+         ((uint32_t)(d & 0xff) << 24);
+}
+
 // MXFP4 block exponent (OCP microscaling, E8M0 range): the smallest X with
 // amax <= 6·2^X, 6 being e2m1's largest value.  With amax = f·2^e,
 // f in [0.5, 1): X = e - 3 + (f > 0.75); clamped to [-127, 127]; amax = 0

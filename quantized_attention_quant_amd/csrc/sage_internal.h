@@ -26,6 +26,10 @@ struct AttnArgs {
   const int32_t* qb_flags = nullptr;
   const int32_t* qb_any = nullptr;
   bool q_per_token = false;  // q_scale holds one scale per query row
+  // per-block Q (neither option): when set, the attention kernel quantises the
+  // fp16 Q itself (q and q_scale unused) with the softmax scale sm_scale
+  const uint16_t* q16 = nullptr;
+  float sm_scale = 0.f;
 };
 
 // MXFP4 attention (the operands of launch_mx_prepare).
