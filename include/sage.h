@@ -207,8 +207,9 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  * sage_test_workspace_layout: byte offsets, inside the sage_attn_fwd
  *   (varlen == 0) or sage_attn_varlen_fwd (varlen != 0) workspace, of
  *   [0] q_int8, [1] k_int8, [2] q_scale, [3] k_scale, [4] k_mean ([0] and [2]
- *   are left unwritten with options 0 in SAGE_PV_FP16 / SAGE_PV_FP8_E4M3
- *   mode: the attention kernel quantises Q itself, with the same quantiser),
+ *   are left unwritten without SAGE_OPT_SMOOTH_Q in SAGE_PV_FP16 /
+ *   SAGE_PV_FP8_E4M3 mode: the attention kernel quantises Q itself, with the
+ *   same quantiser),
  *   [5] packed e4m3 V and [6] v_scale (fp8 mode; both empty in fp16 mode, whose
  *   kernel reads the caller's V directly),
  *   and, with SAGE_OPT_SMOOTH_Q (empty regions otherwise), [7] q_mean fp32
@@ -247,12 +248,12 @@ sage_status_t sage_attn_varlen_fwd(const void* q, const void* k, const void* v, 
  *   workspace that a preceding sage_attn_fwd call with the same B,H,H_kv,N,d,
  *   is_causal, pv_mode and options has filled (its pre-pass results are reused
  *   as they are); writes o fp16 [B,H,N,d] (no LSE).  q: that call's fp16 Q
- *   [B,H,N,d] — with options 0 and SAGE_PV_FP16 or SAGE_PV_FP8_E4M3 the
- *   attention kernel quantises Q itself (the pre-pass then leaves regions [0]
- *   and [2] unwritten), with the default softmax scale; with q NULL in that
- *   mode the kernel instead reads Q̂ and δQ from regions [0] and [2], which the
- *   caller has filled (e.g. with sage_quant_qk's results); ignored, may be
- *   NULL, with options.  v: that call's fp16 V [B,H_kv,N,d] (SAGE_PV_FP16 reads it
+ *   [B,H,N,d] — without SAGE_OPT_SMOOTH_Q, in SAGE_PV_FP16 or
+ *   SAGE_PV_FP8_E4M3 mode, the attention kernel quantises Q itself (the
+ *   pre-pass then leaves regions [0] and [2] unwritten), with the default
+ *   softmax scale; with q NULL in that mode the kernel instead reads Q̂ and δQ
+ *   from regions [0] and [2], which the caller has filled (e.g. with
+ *   sage_quant_qk's results); ignored, may be NULL, with SAGE_OPT_SMOOTH_Q.  v: that call's fp16 V [B,H_kv,N,d] (SAGE_PV_FP16 reads it
  *   directly; ignored, may be NULL, in the other modes).  Used to time the
  *   attention kernel alone.  Same validation as sage_attn_fwd.  SAGE_MXFP4
  *   uses the default softmax scale.

@@ -220,10 +220,10 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   float* fix = reinterpret_cast<float*>(ws + L.off[10]);
   int32_t* flags = reinterpret_cast<int32_t*>(ws + L.off[11]);
 
-  // per-block Q without smoothing: the attention kernel quantises the fp16 Q
-  // itself (the same quantiser), so the pre-pass neither writes nor the
-  // kernel reads Q̂ and δQ
-  const bool qfuse = !sq && !qtok;
+  // Q without smoothing (per block or per token): the attention kernel
+  // quantises the fp16 Q itself (the same quantiser), so the pre-pass neither
+  // writes nor the kernel reads Q̂ and δQ
+  const bool qfuse = !sq;
   sage::launch_quant_qk(g, gk, q, k, sm, qfuse ? nullptr : q8, k8, qfuse ? nullptr : qs, ks, km, qm, qtok, colsum,
                         st);
   int32_t* any = sq ? row_summaries(ws + L.off[11], g.B, g.H, g.N) : nullptr;
@@ -409,9 +409,9 @@ sage_status_t sage_test_attn_from_workspace(void* o, const void* q, const void* 
   if (pv_mode == SAGE_PV_FP16 && (!v || !aligned16(v))) return SAGE_ERR_INVALID_ARGUMENT;
   if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
   if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
-  // per-block Q without smoothing: the attention kernel quantises q itself, or,
-  // with q NULL, reads Q̂ and δQ from regions [0] and [2]
-  const bool qfuse = pv_mode != SAGE_MXFP4 && options == 0 && q != nullptr;
+  // Q without smoothing: the attention kernel quantises q itself, or, with q
+  // NULL, reads Q̂ and δQ from regions [0] and [2]
+  const bool qfuse = pv_mode != SAGE_MXFP4 && (options & SAGE_OPT_SMOOTH_Q) == 0 && q != nullptr;
   if (qfuse && !aligned16(q)) return SAGE_ERR_INVALID_ARGUMENT;
   const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
   const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, pv_mode, options);

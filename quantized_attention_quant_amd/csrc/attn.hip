@@ -685,13 +685,15 @@ void attn_fwd_kernel(AttnArgs a) {
     if (D == 128 && !FP8) asm volatile("" : "+v"(m));
     mg[i] = m;
   }
-  // Per-block Q quantised here (q16 set): the lane's 16-channel runs of its
-  // query in fp32, the wave's largest |x| to LDS; the block's four waves'
-  // maxima are combined after the barrier below.  The codes and scale are
-  // those of the Q pre-pass (the same quantiser, in the same precision).
-  const bool qfuse = QM == kQmBlock && a.q16 != nullptr;
+  // Q quantised here (q16 set): the lane's 16-channel runs of its query in
+  // fp32; per block, the wave's largest |x| goes to LDS and the block's four
+  // waves' maxima are combined after the barrier below; per token, the two
+  // lanes of the row combine theirs.  The codes and scales are those of the Q
+  // pre-pass (the same quantiser, in the same precision).
+  const bool qfuse = (QM == kQmBlock || QM == kQmToken) && a.q16 != nullptr;
   __shared__ float qmax_s[kAttnWaves];
   float qx[DT][16];
+  float qamax = 0.f;  // per-token Q: the lane's row maximum
   float dq = 0.f;
   if (qfuse) {
     float amax = 0.f;
@@ -714,8 +716,12 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < 16; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(qx[ks][j]));
     }
-    amax = wave_max(amax);
-    if (lane == 0) qmax_s[w] = amax;
+    if (QM == kQmToken) {
+      qamax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));  // the row: both lane halves
+    } else {
+      amax = wave_max(amax);
+      if (lane == 0) qmax_s[w] = amax;
+    }
   } else {
     load_q_frags<D>(c.qf, a.q + row0 * D, qrow, n, gg);
     // δQ: the wave's block scale (uniform), or this lane's query's own scale
@@ -759,8 +765,9 @@ void attn_fwd_kernel(AttnArgs a) {
   if (qfuse) {
     // the Q block of this wave: waves 4·(w/4) .. +3
     const int wb0 = w & ~3;
-    const float amax =
-        __builtin_fmaxf(__builtin_fmaxf(qmax_s[wb0], qmax_s[wb0 + 1]), __builtin_fmaxf(qmax_s[wb0 + 2], qmax_s[wb0 + 3]));
+    const float amax = QM == kQmToken ? qamax
+                                      : __builtin_fmaxf(__builtin_fmaxf(qmax_s[wb0], qmax_s[wb0 + 1]),
+                                                        __builtin_fmaxf(qmax_s[wb0 + 2], qmax_s[wb0 + 3]));
     const float s = amax / kInt8Max;
     const float r = 1.0f / s;
 #pragma unroll

@@ -606,7 +606,7 @@ void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const 
                      float* q_mean, bool q_per_token, long long* colsum, hipStream_t st) {
   // gq: Q's geometry (H query heads); gk: K's (its own head count), same
   // sequences.  q_mean != nullptr selects Q smoothing, q_per_token per-token
-  // Q scales (not both); with neither, q_int8 == nullptr leaves Q to the
+  // Q scales (not both); without smoothing, q_int8 == nullptr leaves Q to the
   // attention kernel (it quantises the fp16 Q itself).
   const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q);
   const uint16_t* k16 = reinterpret_cast<const uint16_t*>(k);
@@ -620,10 +620,10 @@ void launch_quant_qk(const SeqGeom& gq, const SeqGeom& gk, const void* q, const 
     if (q_mean)                                                                                                \
       hipLaunchKernelGGL((quant_block_kernel<DD, kQBlock, kShiftBlock>), gqb, blk, 0, st, q16, gq,             \
                          (const long long*)nullptr, sm_scale, q_int8, q_scale, q_mean);                        \
-    else if (q_per_token)                                                                                      \
+    else if (q_per_token && q_int8)                                                                            \
       hipLaunchKernelGGL((quant_row_kernel<DD, kRowsPerBlock>), hs_grid(gq, kRowsPerBlock), blk, 0, st, q16,   \
                          gq, sm_scale, q_int8, q_scale);                                                       \
-    else if (q_int8)                                                                                           \
+    else if (!q_per_token && q_int8)                                                                           \
       hipLaunchKernelGGL((quant_block_kernel<DD, kQBlock, kShiftNone>), gqb, blk, 0, st, q16, gq,              \
                          (const long long*)nullptr, sm_scale, q_int8, q_scale, (float*)nullptr);               \
     hipLaunchKernelGGL((quant_block_kernel<DD, kKBlock, kShiftKMean>), gkb, blk, 0, st, k16, gk, cs, 1.0f,     \

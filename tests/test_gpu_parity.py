@@ -491,28 +491,31 @@ def test_varlen_workload():
         check_out(o[h, a + rows], o1, o2, f"varlen seq={i} n={n} h={h}")
 
 
+@pytest.mark.parametrize("per_token", [False, True])
 @pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n,d", [(1000, 128), (333, 64), (129, 128)])
-def test_in_kernel_q_quantisation_bit_exact(n, d, causal, pv_mode):
-    """Without options the attention kernel quantises Q itself.  Its codes and
-    block scales are the pre-pass's: the same attention run on the pre-pass's
-    Q̂ and δQ (placed in the workspace) gives a bit-identical output."""
-    say(f"case in-kernel Q quantisation n={n} d={d} causal={causal} pv={pv_mode}")
+def test_in_kernel_q_quantisation_bit_exact(n, d, causal, pv_mode, per_token):
+    """Without Q smoothing the attention kernel quantises Q itself (per block,
+    or per token).  Its codes and scales are the pre-pass's: the same attention
+    run on the pre-pass's Q̂ and δQ (placed in the workspace) gives a
+    bit-identical output."""
+    say(f"case in-kernel Q quantisation n={n} d={d} causal={causal} pv={pv_mode} per_token={per_token}")
     B, H = 2, 3
     x = workloads.generate_custom(880 + n + d, B, H, n, d, k_bias=3.0, q_bias=2.0)
     # a few rows of very different magnitude so that block maxima differ
     x.q[:, :, ::97] = (x.q[:, :, ::97].astype(np.float32) * np.float32(9.0)).astype(np.float16)
     q, k, v = dev(x.q), dev(x.k), dev(x.v)
-    ws = torch.empty(sage.sage_attn_workspace_size(B, H, n, d, pv_mode), dtype=torch.uint8, device="cuda")
-    fused = sage.sage_attn_fwd(q, k, v, is_causal=causal, pv_mode=pv_mode, workspace=ws)
-    ref = sage.sage_quant_qk(q, k)
-    offs = sage.sage_test_workspace_layout(False, B, H, n, 0, d, pv_mode)
-    n8, nq = B * H * n * d, B * H * (-(-n // 128))
+    ws = torch.empty(sage.sage_attn_workspace_size(B, H, n, d, pv_mode, q_per_token=per_token), dtype=torch.uint8,
+                     device="cuda")
+    fused = sage.sage_attn_fwd(q, k, v, is_causal=causal, pv_mode=pv_mode, workspace=ws, q_per_token=per_token)
+    ref = sage.sage_quant_qk(q, k, q_per_token=per_token)
+    offs = sage.sage_test_workspace_layout(False, B, H, n, 0, d, pv_mode, q_per_token=per_token)
+    n8, nq = B * H * n * d, B * H * (n if per_token else -(-n // 128))
     ws[offs[0]:offs[0] + n8].copy_(ref["q_int8"].reshape(-1).view(torch.uint8))
     ws[offs[2]:offs[2] + 4 * nq].copy_(ref["q_scale"].reshape(-1).view(torch.uint8))
     from_prepass = torch.empty_like(fused)
-    sage.sage_test_attn_from_workspace(from_prepass, ws, v, is_causal=causal, pv_mode=pv_mode)
+    sage.sage_test_attn_from_workspace(from_prepass, ws, v, is_causal=causal, pv_mode=pv_mode, q_per_token=per_token)
     torch.cuda.synchronize()
     same = torch.equal(fused.view(torch.int16), from_prepass.view(torch.int16))
     say(f"  bit-identical={same}")

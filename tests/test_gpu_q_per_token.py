@@ -78,9 +78,8 @@ def test_q_per_token_small_all_rows(n, d, causal, pv_mode):
     o, lse, wsn = host(o), host(lse), host(ws)
     quant = O.quant_qk_dense(x.q, x.k, q_per_token=True)
     offs = sage.sage_test_workspace_layout(False, B, H, n, 0, d, pv_mode, q_per_token=True)
-    n8 = B * H * n * d
-    assert (wsn[offs[0]:offs[0] + n8].view(np.int8) == quant["q_int8"].ravel()).all()
-    assert (wsn[offs[2]:offs[2] + 4 * B * H * n].view(np.uint32) == quant["q_scale"].view(np.uint32).ravel()).all()
+    # Q̂ and the per-token scales are formed inside the attention kernel (bit
+    # identity with the pre-pass: test_gpu_parity.test_in_kernel_q_quantisation_bit_exact)
     rows = np.arange(n)
     for b in range(B):
         for h in range(H):
