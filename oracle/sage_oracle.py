@@ -78,11 +78,12 @@ FIXED_POINT_SHIFT = 24   # fp16 values are integer multiples of 2^-24
 __all__ = [
     "Q_BLOCK", "K_BLOCK", "KV_TILE", "default_sm_scale", "k_token_mean", "smooth_k",
     "quantize_int8_blocks", "quant_q", "quant_k", "quant_qk_dense", "quant_qk_varlen",
-    "e4m3_decode", "e4m3_encode", "quant_v_fp8", "quant_v_fp8_dense", "quant_v_fp8_varlen",
+    "e4m3_decode", "e4m3_encode", "quant_v_fp8",
     "qk_int", "sage_attention_rows", "sdpa_fp64_rows", "head_views_dense",
     "head_views_varlen", "q_block_mean", "quant_q_smooth", "q_smooth_bias", "quant_q_per_token",
     "E2M1_MAX", "MX_BLOCK", "e2m1_decode", "e2m1_encode", "mx_block_exponent", "mx_quantize",
     "quant_mxfp4_qk", "quant_mxfp4_v", "mxfp4_decode", "mxfp4_attention_rows", "quant_mxfp4_q_smooth",
+    "mxfp4_open_code_bound", "score_lse_rows",
 ]
 
 
@@ -353,25 +354,6 @@ def quant_v_fp8(v: np.ndarray):
     return codes, scale
 
 
-def quant_v_fp8_dense(v: np.ndarray):
-    return quant_v_fp8(v)
-
-
-def quant_v_fp8_varlen(v: np.ndarray, cu_seqlens: Sequence[int]):
-    """Packed [H,T,d] -> codes [H,T,d] and scales [nseq,H,d] (per sequence)."""
-    H, T, d = v.shape
-    cu = np.asarray(cu_seqlens, dtype=np.int64)
-    codes = np.zeros((H, T, d), np.uint8)
-    scales = np.zeros((len(cu) - 1, H, d), np.float32)
-    for i in range(len(cu) - 1):
-        a, b = int(cu[i]), int(cu[i + 1])
-        if b > a:
-            c, s = quant_v_fp8(v[:, a:b])
-            codes[:, a:b] = c
-            scales[i] = s
-    return codes, scales
-
-
 # ----------------------------------------------------------------------------
 # OCP FP4 (e2m1) and microscaling (MX) blocks ([DT] "SageAttention 3":
 # microscaling FP4 attention with two-level quantisation).  e2m1: 1 sign bit,
@@ -465,8 +447,7 @@ def quant_mxfp4_v(v: np.ndarray):
 
 
 def mxfp4_attention_rows(q_codes, q_X, k_codes, k_X, v_codes, v_X, rows: Sequence[int], causal: bool,
-                         sm_scale: float, tile: int = KV_TILE, score_eps: Optional[np.ndarray] = None,
-                         score_bias: Optional[np.ndarray] = None):
+                         sm_scale: float, tile: int = KV_TILE, score_bias: Optional[np.ndarray] = None):
     """Output rows of the MXFP4 attention for one (sequence, head).
 
     S = (Q̃ K̃ᵀ)·sm_scale with Q̃, K̃ the decoded MX FP4 values; online softmax
@@ -474,10 +455,6 @@ def mxfp4_attention_rows(q_codes, q_X, k_codes, k_X, v_codes, v_X, rows: Sequenc
     level one: p = e^(s - m) <= 1; level two: per query and 32-key block,
     p̃ = e2m1(p / 2^X)·2^X with X from the block's largest p; O = αO + P̃·Ṽ;
     out = fp16(O / l), l from the unrounded p.  fp64 arithmetic.
-
-    ``score_eps`` [n] (natural-log units, per key): as for the fp8 path, the
-    P codes (and block exponents) a score moved by at most ε may take are
-    left open; then (out, bound) is returned, bound fp64 [len(rows), d].
     ``score_bias`` [ceil(n/128), n]: a term added to the scores of each Q
     block's rows, as in ``sage_attention_rows``.
     """
@@ -490,6 +467,59 @@ def mxfp4_attention_rows(q_codes, q_X, k_codes, k_X, v_codes, v_X, rows: Sequenc
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     O = np.zeros((R, d))
+    last_row = int(rows.max()) if R else -1
+    with np.errstate(invalid="ignore", over="ignore", divide="ignore"):
+        for t0 in range(0, n, tile):
+            if causal and t0 > last_row:
+                break
+            keys = np.arange(t0, min(n, t0 + tile))
+            s = (qv @ kv[keys].T) * float(sm_scale)
+            if score_bias is not None:
+                s = s + score_bias[rows // Q_BLOCK][:, keys]
+            if causal:
+                s = np.where(keys[None, :] > rows[:, None], -np.inf, s)
+            m_new = np.maximum(m, s.max(axis=1))
+            live = m_new > -np.inf
+            alpha = np.where(live, np.exp(m - m_new), 1.0)
+            alpha = np.where(np.isneginf(m) & live, 0.0, alpha)
+            p = np.where(live[:, None], np.exp(s - m_new[:, None]), 0.0)
+            l = alpha * l + p.sum(axis=1)
+            pq = np.zeros_like(p)
+            for b0 in range(0, len(keys), MX_BLOCK):       # 32-key blocks of the tile
+                sl = slice(b0, b0 + MX_BLOCK)
+                X = mx_block_exponent(p[:, sl].max(axis=1))[:, None]
+                pq[:, sl] = e2m1_decode(e2m1_encode(p[:, sl] * np.ldexp(1.0, -X))) * np.ldexp(1.0, X)
+            O = alpha[:, None] * O + pq @ vv[keys]
+            m = m_new
+    return (O / l[:, None]).astype(np.float16)
+
+
+def mxfp4_open_code_bound(q_codes, q_X, k_codes, k_X, v_codes, v_X, rows: Sequence[int], causal: bool,
+                          sm_scale: float, score_eps: np.ndarray, tile: int = KV_TILE,
+                          score_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Per output element of ``mxfp4_attention_rows``, the largest change that
+    another correct evaluation of the scores can make through the P codes.
+
+    P is quantised to 3-bit e2m1 elements with a per-block power-of-two scale
+    taken from the block's largest p, so a score moved by a rounding-size ε (an
+    fp32 evaluation against this fp64 one) can move a code, or a block's
+    exponent, to a neighbour — each such choice is the method.  With ε per key
+    (``score_eps`` [n], natural-log units), p moves by at most e^(±2ε) (ε from
+    the score and ε from the tile max it is taken against); e2m1 rounding and
+    the exponent choice are monotone, so every code lies between those of the
+    two ends.  Returns fp64 [len(rows), d]: (W + γ·(W + 2·Wabs)) / l with W the
+    running sum of |code change|·|Ṽ|, Wabs of |P̃|·|Ṽ| and γ = e^(4ε_max) - 1
+    for the row sums.  Test infrastructure: the reference itself is
+    ``mxfp4_attention_rows``.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    n, d = k_codes.shape
+    R = len(rows)
+    qv = mxfp4_decode(q_codes[rows], q_X[rows], -1)
+    kv = mxfp4_decode(k_codes, k_X, -1)
+    vv = np.abs(mxfp4_decode(v_codes, v_X, -2))
+    m = np.full(R, -np.inf)
+    l = np.zeros(R)
     W = np.zeros((R, d))
     Wabs = np.zeros((R, d))
     last_row = int(rows.max()) if R else -1
@@ -511,30 +541,25 @@ def mxfp4_attention_rows(q_codes, q_X, k_codes, k_X, v_codes, v_X, rows: Sequenc
             l = alpha * l + p.sum(axis=1)
             pq = np.zeros_like(p)
             dcode = np.zeros_like(p)
-            for b0 in range(0, len(keys), MX_BLOCK):       # 32-key blocks of the tile
+            for b0 in range(0, len(keys), MX_BLOCK):
                 sl = slice(b0, b0 + MX_BLOCK)
                 pb = p[:, sl]
                 X = mx_block_exponent(pb.max(axis=1))[:, None]
                 pq[:, sl] = e2m1_decode(e2m1_encode(pb * np.ldexp(1.0, -X))) * np.ldexp(1.0, X)
-                if score_eps is not None:
-                    e2 = 2.0 * score_eps[keys[sl]][None, :]
-                    cands = []
-                    for ps in (pb * np.exp(-e2), pb * np.exp(e2)):
-                        for Xc in (mx_block_exponent(ps.max(axis=1))[:, None],
-                                   mx_block_exponent((pb * np.exp(-e2)).max(axis=1))[:, None],
-                                   mx_block_exponent((pb * np.exp(e2)).max(axis=1))[:, None]):
-                            cands.append(e2m1_decode(e2m1_encode(ps * np.ldexp(1.0, -Xc))) * np.ldexp(1.0, Xc))
-                    dcode[:, sl] = np.max([np.abs(c - pq[:, sl]) for c in cands], axis=0)
-            O = alpha[:, None] * O + pq @ vv[keys]
-            if score_eps is not None:
-                W = alpha[:, None] * W + dcode @ np.abs(vv[keys])
-                Wabs = alpha[:, None] * Wabs + pq @ np.abs(vv[keys])
+                e2 = 2.0 * score_eps[keys[sl]][None, :]
+                lo, hi = pb * np.exp(-e2), pb * np.exp(e2)
+                cands = []
+                for ps in (lo, hi):
+                    for Xc in (mx_block_exponent(ps.max(axis=1))[:, None],
+                               mx_block_exponent(lo.max(axis=1))[:, None],
+                               mx_block_exponent(hi.max(axis=1))[:, None]):
+                        cands.append(e2m1_decode(e2m1_encode(ps * np.ldexp(1.0, -Xc))) * np.ldexp(1.0, Xc))
+                dcode[:, sl] = np.max([np.abs(c - pq[:, sl]) for c in cands], axis=0)
+            W = alpha[:, None] * W + dcode @ vv[keys]
+            Wabs = alpha[:, None] * Wabs + pq @ vv[keys]
             m = m_new
-    out = O / l[:, None]
-    if score_eps is not None:
-        gamma = np.expm1(4.0 * np.max(score_eps))
-        return out.astype(np.float16), (W + gamma * (W + 2.0 * Wabs)) / l[:, None]
-    return out.astype(np.float16)
+    gamma = np.expm1(4.0 * np.max(score_eps))
+    return (W + gamma * (W + 2.0 * Wabs)) / l[:, None]
 
 
 # ----------------------------------------------------------------------------
@@ -557,21 +582,15 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
                         k_scale: np.ndarray, v: np.ndarray, rows: Sequence[int], causal: bool,
                         pv_mode: str = "fp16", v_scale: Optional[np.ndarray] = None,
                         tile: int = KV_TILE, score_bias: Optional[np.ndarray] = None,
-                        score_eps: Optional[np.ndarray] = None, q_block: int = Q_BLOCK):
+                        q_block: int = Q_BLOCK):
     """Output rows of the quantised attention for one (sequence, head).
 
     Inputs: q_int8/k_int8 [n, d] codes, q_scale [ceil(n/q_block)] (softmax
-    scale folded in; q_block = 1 for per-token Q scales), k_scale [ceil(n/64)]; v fp16 [n, d] (fp16 mode) or e4m3 codes
-    [n, d] with v_scale [d] (fp8 mode).  ``rows``: query indices.
-    ``score_bias``: with a smoothed Q, the [ceil(n/128), n] term of
-    ``q_smooth_bias``, added to every score of a row of that Q block.
-    ``score_eps`` (fp8 mode): a [ceil(n/128), n] bound on how far another
-    correct evaluation may move each score (natural-log units).  Every P code
-    whose 448·p could then round to a neighbouring e4m3 value is a code the
-    method leaves open; the function also returns, per output element, the
-    largest change such a choice of codes, together with the ε-size change
-    of the row sum, can make (fp64 [len(rows), d]), so that a comparison can
-    accept exactly those outputs.
+    scale folded in; q_block = 1 for per-token Q scales), k_scale [ceil(n/64)];
+    v fp16 [n, d] (fp16 mode) or e4m3 codes [n, d] with v_scale [d] (fp8
+    mode).  ``rows``: query indices.  ``score_bias``: with a smoothed Q, the
+    [ceil(n/128), n] term of ``q_smooth_bias``, added to every score of a row
+    of that Q block.
 
     Steps:
       * S = int(Q̂K̂ᵀ) · δQ · δK  ([PS] quantisation step 3, C ≈ (ÂB̂)(δAδB)),
@@ -602,8 +621,6 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
     m = np.full(R, -np.inf)
     l = np.zeros(R)
     O = np.zeros((R, d))
-    W = np.zeros((R, d))       # bound on |O - O'| over the open P codes (fp8 with score_eps)
-    Wabs = np.zeros((R, d))    # the same sum of P̂·V̂ in absolute values
     last_row = int(rows.max()) if R else -1
     with np.errstate(invalid="ignore", over="ignore"):
         for t0 in range(0, n, tile):
@@ -630,28 +647,11 @@ def sage_attention_rows(q_int8: np.ndarray, q_scale: np.ndarray, k_int8: np.ndar
                 pq = e4m3_decode(e4m3_encode(p * E4M3_MAX))
                 A = pq @ vv[keys]                       # level 1: this tile only
                 O = alpha[:, None] * O + A              # level 2: running output
-                if score_eps is not None:
-                    # p moves by at most a factor e^(±2ε): ε from the score and ε
-                    # from the tile max it is taken against; e4m3 rounding is
-                    # monotone, so the code stays between those of the ends
-                    e2 = 2.0 * score_eps[rows // Q_BLOCK][:, keys]
-                    lo = e4m3_decode(e4m3_encode(p * E4M3_MAX * np.exp(-e2)))
-                    hi = e4m3_decode(e4m3_encode(np.minimum(p * E4M3_MAX * np.exp(e2), E4M3_MAX)))
-                    dcode = np.maximum(np.abs(hi - pq), np.abs(pq - lo))
-                    W = alpha[:, None] * W + dcode @ np.abs(vv[keys])
-                    Wabs = alpha[:, None] * Wabs + pq @ np.abs(vv[keys])
             m = m_new
     if pv_mode == "fp16":
         out = O / l[:, None]
     else:
         out = O * v_scale.astype(np.float64)[None, :] / (E4M3_MAX * l[:, None])
-        if score_eps is not None:
-            # each tile's share is weighted by e^(m_t - m_final) and the row
-            # sum by e^(±2ε) as well: with γ = e^(4ε) - 1 over the row,
-            # |out' - out| <= (W + γ·(W + 2·Wabs))·δV / (448·l)
-            gamma = np.expm1(4.0 * score_eps[rows // Q_BLOCK].max(axis=1))[:, None]
-            bound = (W + gamma * (W + 2.0 * Wabs)) * v_scale.astype(np.float64)[None, :] / (E4M3_MAX * l[:, None])
-            return out.astype(np.float16), bound
     return out.astype(np.float16)
 
 

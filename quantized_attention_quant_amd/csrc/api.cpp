@@ -172,6 +172,11 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   if (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(o, tensor_bytes, k, kv_bytes) ||
       overlaps(o, tensor_bytes, v, kv_bytes) || overlaps(o, tensor_bytes, workspace, L.total))
     return SAGE_ERR_INVALID_ARGUMENT;
+  // the kernels read q, k and v after the pre-pass has written the workspace
+  // (fp16 V in place, K again for the smoothing term, Q in the attention kernel)
+  if (overlaps(workspace, L.total, q, tensor_bytes) || overlaps(workspace, L.total, k, kv_bytes) ||
+      overlaps(workspace, L.total, v, kv_bytes))
+    return SAGE_ERR_INVALID_ARGUMENT;
   if (lse && (overlaps(lse, lse_bytes, o, tensor_bytes) || overlaps(lse, lse_bytes, q, tensor_bytes) ||
               overlaps(lse, lse_bytes, k, kv_bytes) || overlaps(lse, lse_bytes, v, kv_bytes) ||
               overlaps(lse, lse_bytes, workspace, L.total)))
@@ -226,8 +231,15 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
   const bool qfuse = !sq;
   sage::launch_quant_qk(g, gk, q, k, sm, qfuse ? nullptr : q8, k8, qfuse ? nullptr : qs, ks, km, qm, qtok, colsum,
                         st);
-  int32_t* any = sq ? row_summaries(ws + L.off[11], g.B, g.H, g.N) : nullptr;
-  if (sq) {
+  int32_t* any = sq && !fp8 ? row_summaries(ws + L.off[11], g.B, g.H, g.N) : nullptr;
+  if (sq && fp8) {
+    // FP8 PV: every key's term in fp32, sm_scale·q̄·x·log2(e), in region [10]
+    sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, nullptr, qm, nullptr, reinterpret_cast<int32_t*>(fix),
+                       nullptr, nullptr, nullptr, g, g.H / Hkv, (float)((double)sm * 1.4426950408889634),
+                       is_causal != 0};
+    qa.raw = 1;
+    sage::launch_q_bias(qa, st);
+  } else if (sq) {
     sage::launch_zero(any, align16(sizeof(int32_t) * (size_t)g.B * g.H * ceil_div64(g.N, sage::kQBlock)), st);
     const sage::QBiasArgs qa{static_cast<const uint16_t*>(k), km, ks, qm, qs, slots, fix, flags, any, g, g.H / Hkv,
                              (float)((double)sm * 1.4426950408889634), is_causal != 0};
@@ -246,9 +258,10 @@ sage_status_t attn_forward(const void* q, const void* k, const void* v, void* o,
     a.sm_scale = sm;
   }
   if (sq) {
-    a.qb_slots = slots;
+    // FP8 PV streams the fp32 terms with the tiles in place of initial values
+    a.qb_slots = fp8 ? reinterpret_cast<const int32_t*>(fix) : slots;
     a.qb_fix = fix;
-    a.qb_flags = flags;
+    a.qb_flags = fp8 ? nullptr : flags;
     a.qb_any = any;
   }
   sage::launch_attn(a, is_causal != 0, fp8, st);
@@ -313,6 +326,28 @@ sage_status_t sage_quant_qk(const void* q, const void* k, int B, int H, int N, i
   float sm;
   if (!resolve_sm_scale(sm_scale, d, &sm)) return SAGE_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < sage_quant_qk_workspace_size(g.B, H, d)) return SAGE_ERR_WORKSPACE_TOO_SMALL;
+  {
+    // the pre-pass reads q and k while it writes the codes, scales and means
+    const bool qtok = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
+    const int64_t rows = cu_seqlens ? (int64_t)H * total_tokens : (int64_t)B * H * N;
+    const size_t nq = (size_t)B * H * ceil_div64(N, sage::kQBlock), nk = (size_t)B * H * ceil_div64(N, sage::kKBlock);
+    const struct {
+      const void* p;
+      size_t n;
+    } r[] = {{q, (size_t)rows * d * 2},
+             {k, (size_t)rows * d * 2},
+             {q_int8, (size_t)rows * d},
+             {k_int8, (size_t)rows * d},
+             {q_scale, sizeof(float) * (qtok ? (size_t)rows : nq)},
+             {k_scale, sizeof(float) * nk},
+             {k_mean, sizeof(float) * (size_t)B * H * d},
+             {q_mean, q_mean ? sizeof(float) * nq * d : 0},
+             {workspace, sage_quant_qk_workspace_size(g.B, H, d)}};
+    constexpr int kRegions = sizeof(r) / sizeof(r[0]);
+    for (int i = 2; i < kRegions; ++i)  // every output and the workspace against everything before it
+      for (int j = 0; j < i; ++j)
+        if (r[i].n && r[j].n && overlaps(r[i].p, r[i].n, r[j].p, r[j].n)) return SAGE_ERR_INVALID_ARGUMENT;
+  }
   if (cu_seqlens && total_tokens == 0) return SAGE_OK;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   sage::launch_quant_qk(g, g, q, k, sm, q_int8, k_int8, q_scale, k_scale, k_mean, q_mean,
@@ -417,8 +452,11 @@ sage_status_t sage_test_attn_from_workspace(void* o, const void* q, const void* 
   const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, pv_mode, options);
   if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
   const size_t tensor_bytes = (size_t)B * H * N * d * 2;
+  const size_t kv_bytes = tensor_bytes / (size_t)H * (size_t)H_kv;
   if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (pv_mode == SAGE_PV_FP16 && overlaps(o, tensor_bytes, v, tensor_bytes / (size_t)H * (size_t)H_kv))
+  if (pv_mode == SAGE_PV_FP16 && (overlaps(o, tensor_bytes, v, kv_bytes) || overlaps(workspace, L.total, v, kv_bytes)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (qfuse && (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(workspace, L.total, q, tensor_bytes)))
     return SAGE_ERR_INVALID_ARGUMENT;
   const char* ws = static_cast<const char*>(workspace);
   const SeqGeom g{nullptr, B, H, N, d, 0};
@@ -443,10 +481,10 @@ sage_status_t sage_test_attn_from_workspace(void* o, const void* q, const void* 
     resolve_sm_scale(0.f, d, &a.sm_scale);
   }
   if (options & SAGE_OPT_SMOOTH_Q) {
-    a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[9]);
+    a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[fp8 ? 10 : 9]);
     a.qb_fix = reinterpret_cast<const float*>(ws + L.off[10]);
-    a.qb_flags = reinterpret_cast<const int32_t*>(ws + L.off[11]);
-    a.qb_any = row_summaries(const_cast<char*>(ws) + L.off[11], B, H, N);
+    a.qb_flags = fp8 ? nullptr : reinterpret_cast<const int32_t*>(ws + L.off[11]);
+    a.qb_any = fp8 ? nullptr : row_summaries(const_cast<char*>(ws) + L.off[11], B, H, N);
   }
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   sage::launch_attn(a, is_causal != 0, fp8, st);

@@ -40,11 +40,14 @@
 //     of the same head (K̂/V reuse in that XCD's L2); heavier causal blocks go
 //     first.
 //   * Smoothed Q (dtcms summary, "SageAttention 2"; smooth_q.hip forms the
-//     term): the part of each score that Q's block mean carries enters as the
-//     accumulator's initial value — magic bias plus that term in units of the
-//     tile's δQ·δK, streamed into LDS with the tile — so the softmax does no
-//     extra work; half tiles whose term does not fit that integer range add it
-//     in fp32 instead (rare: a flag per half tile).
+//     term): the part of each score that Q's block mean carries is streamed
+//     into LDS with the tile.  FP16 PV: it enters as the accumulator's initial
+//     value — magic bias plus that term in units of the tile's δQ·δK — so the
+//     softmax does no extra work; half tiles whose term does not fit that
+//     integer range add it in fp32 instead (rare: a flag per half tile).  FP8
+//     PV: the softmax adds every key's term in fp32 (log2 units), since the P
+//     codes follow the scores closely enough that a term rounded to one unit
+//     of δQ·δK would move some of them.
 #include "sage_common.h"
 #include "sage_internal.h"
 
@@ -417,6 +420,25 @@ __device__ __forceinline__ float exp_pack_fp8(const float (&F)[2][16], float mx,
   return lsum;
 }
 
+// FP8 PV with a smoothed Q: the scores X are already in log2 units (the
+// smoothing term added in fp32); p·448 = 2^(X + cterm), cterm = log2 448 - m.
+__device__ __forceinline__ float exp_pack_fp8_log2(const float (&X)[2][16], float cterm, v8i& pk) {
+  float lsum = -0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int s = q >> 2, i0 = 4 * (q & 3);
+    float p[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(X[s][i0 + j] + cterm);
+      lsum += p[j];
+    }
+    int wv = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], pk[q], false);
+    pk[q] = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], wv, true);
+  }
+  return lsum;
+}
+
 // O += P·V for one group of 32 queries.  FP8: level 1 (one tile's 64 keys)
 // and level 2 (the running output) are one fp32 MFMA per d tile.
 template <int D, bool FP8>
@@ -536,8 +558,13 @@ __device__ __forceinline__ float row_max(const float (&F)[2][16]) {
 // SM (smoothed Q): F is either magic-biased (M = 1.5·2^23) or, in a tile that
 // took the fp32 path, already the score in log2 units (c2 = 1, M = 0), so the
 // row max starts from -inf and the tile max is (max F - M)·c2.
+//
+// FP8 with a smoothed Q (lterm != nullptr): the scores are magic-biased
+// integers and lterm holds, for this lane's 32 keys, the smoothing term in
+// log2 units (fp32); s = (F - M)·c2 + term, exact max per tile as above.
 template <int D, bool FP8, bool SM = false>
-__device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2, float M = kMagicF) {
+__device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2, float M = kMagicF,
+                                              const float4* __restrict__ lterm = nullptr) {
   float F[2][16];
 #pragma unroll
   for (int s = 0; s < 2; ++s)
@@ -560,6 +587,26 @@ __device__ __forceinline__ void softmax_phase(WaveCtx<D, FP8>& c, float c2, floa
       c.m_run = m_new;
       lsum = exp_pack_fp16(F, c2, m_new, c.pk16, SM ? M : kMagicF);
     }
+    c.l_run += lsum;
+  } else if (SM && lterm) {
+    // lane (r32, g) reg 4q + j of S[s] is key 32s + 8q + 4g + j: lterm[16s + 2q]
+    // (already offset by g) holds those four keys' terms
+    float X[2][16];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 tv = lterm[16 * s + 2 * q];
+        const float t4[4] = {tv.x, tv.y, tv.z, tv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) X[s][4 * q + j] = __builtin_fmaf(F[s][4 * q + j] - M, c2, t4[j]);
+      }
+    float m_new = __builtin_fmaxf(c.m_run, row_max<true>(X));
+    m_new = (m_new == -__builtin_inff()) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(c.m_run - m_new);
+    const float lsum = exp_pack_fp8_log2(X, kLog2E4M3Max - m_new, c.pk8);
+    if (__any(alpha != 1.f)) rescale_o<D>(c.O, c.l_run, alpha);
+    c.m_run = m_new;
     c.l_run += lsum;
   } else {
     float mx = SM ? row_max<true>(F) : row_max(F);
@@ -730,7 +777,8 @@ void attn_fwd_kernel(AttnArgs a) {
   const float* __restrict__ ksc = a.k_scale + hsk * nkb;
   // smoothed Q: whether any half tile of this wave's Q block falls back (rare);
   // only then are the per-tile flags read
-  const bool row_fb = SM && load_uniform_i(a.qb_any, hs * nqb + wqb_in) != 0;
+  // (FP16 PV only: with FP8 PV every key's term is fp32, staged with the tile)
+  const bool row_fb = SM && !FP8 && load_uniform_i(a.qb_any, hs * nqb + wqb_in) != 0;
   c.m_run = -__builtin_inff();
   c.l_run = 0.f;
 #pragma unroll
@@ -798,14 +846,13 @@ void attn_fwd_kernel(AttnArgs a) {
       const bool full = (k0 + kKBlock <= n) && (!CAUSAL || k0 + kKBlock - 1 <= wq_lo);
       if (!full) mask_scores<CAUSAL>(c.S, k0, n, qrow, gg);
       float M = kMagicF;
-      if (SM && row_fb) {
+      if (SM && !FP8 && row_fb) {
         const int64_t row = hs * nqb + wqb;
         const v2i fb = load_uniform2(a.qb_flags, row * (2 * nkb) + 2 * u);
         if (fb.x | fb.y) {
           // a half tile whose smoothing term did not fit the accumulator:
           // every score of the tile becomes fp32 log2 units, s = (F - M)·c2
-          // (+ the fp32 term of a fallback half)
-          const float base = -(kMagicF * c2);
+          // (+ the fp32 term of a fallback half); F - M is exact
           const float* fx = a.qb_fix + row * npad + k0;
 #pragma unroll
           for (int s = 0; s < 2; ++s) {
@@ -818,7 +865,7 @@ void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
                 const int bits = c.S[s][4 * q + j];
-                c.S[s][4 * q + j] = __float_as_int(__builtin_fmaf(__int_as_float(bits), c2, av[j] + base));
+                c.S[s][4 * q + j] = __float_as_int(__builtin_fmaf(__int_as_float(bits) - kMagicF, c2, av[j]));
               }
             }
           }
@@ -843,7 +890,11 @@ void attn_fwd_kernel(AttnArgs a) {
         M = 0.f;
       }
       // FP16 takes the scores' bias at run time (magic-biased, or log2 units)
-      softmax_phase<D, FP8, SM || !FP8>(c, c2, M);
+      const float4* lterm = nullptr;
+      if (SM && FP8)
+        lterm = reinterpret_cast<const float4*>(smem + (u & (kRingStages - 1)) * G::STAGE + G::KBYTES + G::VBYTES) +
+                32 * (wqb - q0 / kQBlock) + gg;
+      softmax_phase<D, FP8, SM || !FP8>(c, c2, M, lterm);
     }
   };
   // One workgroup barrier per tile.  Group A runs matrix(t) then softmax(t),
@@ -863,10 +914,12 @@ void attn_fwd_kernel(AttnArgs a) {
       const int kst = __builtin_amdgcn_readfirstlane((t % kRingStages) * G::STAGE);
       static_assert((kRingStages & (kRingStages - 1)) == 0, "ring index by mask");
       const int vst = (t > 0 ? (t - 1) & (kRingStages - 1) : 0) * G::STAGE;
-      matrix_both<D, FP8, SM>(smem + kst, kofs, smem + vst + G::KBYTES, lane, gg, c.qf, c.S, c.pk16, c.pk8, c.O,
-                              reinterpret_cast<const v4i*>(smem + kst + G::KBYTES + G::VBYTES) +
-                                  32 * (wqb - q0 / kQBlock),
-                              (D == 128 && !FP8) ? &mg : nullptr);
+      // FP8 with a smoothed Q: the accumulator starts at the bias alone (its term is added in fp32)
+      matrix_both<D, FP8, SM && !FP8>(smem + kst, kofs, smem + vst + G::KBYTES, lane, gg, c.qf, c.S, c.pk16, c.pk8,
+                                      c.O,
+                                      reinterpret_cast<const v4i*>(smem + kst + G::KBYTES + G::VBYTES) +
+                                          32 * (wqb - q0 / kQBlock),
+                                      (D == 128 && !FP8) ? &mg : nullptr);
     }
     if (lead) softmax_step(t);
     // tile t+1 landed before anyone's next matrix phase (later tiles may fly)

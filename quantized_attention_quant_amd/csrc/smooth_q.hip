@@ -25,15 +25,19 @@
 //     (cleared before the launch) becomes nonzero when some half of block b
 //     falls back, so the attention kernel reads the flags of that row only.
 //
-// MXFP4 (raw): the scores accumulate in fp32, so the term needs no integer
-// form: slots[hs][b][j] holds q̄_b · x_j itself (fp32 bits, raw score units,
-// before the softmax scale) for every key, and no flags are written.
+// raw (MXFP4 and FP8 PV): the term is used in fp32, with no integer form:
+// slots[hs][b][j] holds q̄_b · x_j · sm_log2e (fp32 bits) for every key, and no
+// flags are written.  MXFP4 passes sm_log2e = 1 (raw score units: its kernel
+// applies the softmax scale to the whole score); FP8 PV passes the softmax
+// scale times log2(e), so the value is the term in the kernel's log2 units.
 //
 // The contraction q̄_b · x_j runs on the fp16 MFMA.  Both operands are scaled
 // by powers of two into [-1, 1] (q̄_b by 2^-eq_b from its largest channel, x_j
-// by 2^-ek_t from its K block's scale) and split into fp16 hi + lo parts;
-// hi·hi + hi·lo + lo·hi keeps about 22 significant bits, with fp32
-// accumulation — far below the INT8 quantisation error of the scores.
+// by 2^-ek_t from its K block's scale, or in raw mode from its wave's largest
+// |x|) and split into fp16 hi + lo parts (about 22 significant bits each);
+// hi·hi + hi·lo + lo·hi, plus lo·lo in raw mode, with fp32 accumulation —
+// far below the INT8 quantisation error of the scores, and in raw mode close
+// to an fp32 evaluation.
 #include "sage_common.h"
 #include "sage_internal.h"
 
@@ -208,13 +212,15 @@ __global__ __launch_bounds__(kThreads) void q_bias_kernel(QBiasArgs a) {
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[kk], bhi, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(ahi[kk], blo, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[kk], bhi, acc, 0, 0, 0);
+        // fp32 terms (FP8 P codes, MXFP4 scores) keep the lo·lo part as well
+        if (a.raw) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(alo[kk], blo, acc, 0, 0, 0);
       }
       // lane holds Q block bb = 32·grp + r32 for keys kw0 + 8(i/4) + 4gg + i%4
       const int bb = grp * kQbBlocksPerGroup + r32;
       const bool blk_live = bb < nqb_seq && !(a.causal && kKBlock * t > kQBlock * bb + kQBlock - 1);
       const float f = ldexpf(a.sm_log2e, eq_s[r32] + ek);
       if (a.raw) {
-        // q̄·x in raw score units (sm_log2e = 1 here), every key, no flags
+        // q̄·x·sm_log2e, every key, no flags
         if (blk_live) {
           const int64_t rowoff = (hs * nqb + bb) * (int64_t)npad;
 #pragma unroll

@@ -130,6 +130,9 @@ def _fwd(**over):
     (dict(sm=float("inf")), INVALID),
     (dict(wsb=100), WS_SMALL),
     (dict(o=ALIGNED), INVALID),              # output aliases q
+    (dict(ws=ALIGNED), INVALID),             # workspace aliases q
+    (dict(ws=ALIGNED * 2), INVALID),         # workspace aliases k
+    (dict(ws=ALIGNED * 3, o=ALIGNED * 16), INVALID),  # workspace aliases v
     (dict(Hkv=0), INVALID),
     (dict(Hkv=3), INVALID),                  # does not divide H
     (dict(Hkv=4), INVALID),                  # more K/V heads than query heads
@@ -177,6 +180,12 @@ def test_quant_rejects():
     assert quant(options=1) == INVALID                              # Q smoothing without q_mean
     assert quant(q_mean=ALIGNED * 7, options=3) == UNSUPPORTED      # smoothing + per-token scales
     assert quant(options=8) == INVALID                              # unknown option bit
+    assert quant(q_int8=ALIGNED) == INVALID                         # Q codes over the fp16 Q
+    assert quant(q_int8=ALIGNED * 2 + 4096) == INVALID              # Q codes inside the fp16 K
+    assert quant(q_int8=ALIGNED * 8 + 256, wsb=1 << 20) == INVALID  # Q codes inside the workspace
+    st = L.sage_quant_qk(ALIGNED, ALIGNED * 2, 1, 2, 256, 64, 0, None, 0, 0.0, ALIGNED * 9, ALIGNED * 3,
+                         ALIGNED * 9 + 1024, ALIGNED * 5, ALIGNED * 6, None, 0, ALIGNED * 8, 1 << 20, None)
+    assert st == INVALID                                            # Q scales inside the Q codes
     st = L.sage_quant_v_fp8(ALIGNED, 1, 2, 256, 100, 0, None, 0, ALIGNED * 2, ALIGNED * 3, None)
     assert st == INVALID
     st = L.sage_test_qk_tiles(ALIGNED, ALIGNED * 2, 1, 1, 128, 64, ALIGNED * 3, 0, ALIGNED * 4, None)
@@ -184,6 +193,19 @@ def test_quant_rejects():
     arr = (ctypes.c_size_t * 12)()
     assert L.sage_test_workspace_layout(0, 1, 1, 1, 128, 0, 80, 0, 0, arr) == INVALID
     assert L.sage_test_workspace_layout(0, 1, 4, 3, 128, 0, 64, 0, 0, arr) == INVALID
+
+
+def test_attn_from_workspace_rejects_aliasing():
+    L = sage.lib()
+    f = L.sage_test_attn_from_workspace
+    # o, q, v, B, H, H_kv, N, d, causal, pv, options, workspace, bytes, stream
+    ok = [ALIGNED * 4, ALIGNED, ALIGNED * 3, 1, 2, 2, 256, 64, 0, 0, 0, ALIGNED * 8, 1 << 30, None]
+    bad = list(ok); bad[11] = ALIGNED * 3            # workspace over the fp16 V the kernel reads
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[11] = ALIGNED                # workspace over the fp16 Q the kernel quantises
+    assert f(*bad) == INVALID
+    bad = list(ok); bad[0] = ALIGNED                 # output over that Q
+    assert f(*bad) == INVALID
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -20,6 +20,7 @@ import pytest
 import torch
 
 import quantized_attention_quant_amd as sage
+import margins
 import workloads
 from oracle import sage_oracle as O
 
@@ -84,6 +85,7 @@ def test_max_sequence_causal_fp16():
     err = np.abs(ours - o1).max()
     c1 = float((ours.ravel() @ o1.ravel()) / (np.linalg.norm(ours) * np.linalg.norm(o1)))
     say(f"  sampled rows: max_abs_vs_O1={err:.3e} cos_O1={c1:.6f}")
+    margins.record("max-size sampled rows", err, c1)
     assert np.isfinite(ours).all()
     assert err <= MAX_ABS and c1 >= COS_O1, (err, c1)
 

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import quantized_attention_quant_amd as sage
+import margins
 import workloads
 from oracle import sage_oracle as O
 
@@ -99,8 +100,9 @@ def o1_rows(qq, vq, b, h, rows, causal, sm, v_rep_h=None):
     kv = O.mxfp4_decode(kc[b, h], kx[b, h], -1)
     smax = np.abs(qv[rows]).sum(axis=1).max() * np.abs(kv).max() * sm
     eps = np.full(kc.shape[2], 4e-6 * (1.0 + smax))
-    o1, bound = O.mxfp4_attention_rows(qc[b, h], qx[b, h], kc[b, h], kx[b, h], vc[b, h], vx[b, h], rows, causal, sm,
-                                       score_eps=eps)
+    args = (qc[b, h], qx[b, h], kc[b, h], kx[b, h], vc[b, h], vx[b, h], rows, causal, sm)
+    o1 = O.mxfp4_attention_rows(*args)
+    bound = O.mxfp4_open_code_bound(*args, score_eps=eps)
     lse = O.score_lse_rows(qv, np.full(len(qv), sm), kv, np.ones(-(-len(kv) // 64)), rows, causal, q_block=1)
     return o1, bound, lse
 
@@ -113,6 +115,7 @@ def check_out(ours, o1, o2, label, bound):
     c1, c2, c12 = cos(ours, o1), cos(ours, o2), cos(o1, o2)
     say(f"{label}: max_abs_vs_O1={diff.max():.3e} (beyond open codes {over:.3e}) cos_O1={c1:.6f} "
         f"cos_O2={c2:.6f} (method {c12:.6f})")
+    margins.record(label, diff.max(), c1, c2)
     assert over <= MAX_ABS, (label, over)
     assert c1 >= COS_O1, (label, c1)
     assert c2 >= c12 - 1e-3, (label, c2, c12)
@@ -252,7 +255,8 @@ def o1_smooth_rows(qs, qsx, qm, kq, vq, k_head, b, h, rows, causal, sm):
     smax = np.abs(qv[rows]).sum(axis=1).max() * np.abs(kv).max() * sm
     tmax = sm * term_tol(qm, k_head, km).max()
     eps = np.full(kc.shape[0], 4e-6 * (1.0 + smax + np.abs(bias).max()) + tmax)
-    o1, bound = O.mxfp4_attention_rows(qs, qsx, kc, kx, vc, vx, rows, causal, sm, score_eps=eps, score_bias=bias)
+    o1 = O.mxfp4_attention_rows(qs, qsx, kc, kx, vc, vx, rows, causal, sm, score_bias=bias)
+    bound = O.mxfp4_open_code_bound(qs, qsx, kc, kx, vc, vx, rows, causal, sm, score_eps=eps, score_bias=bias)
     lse = O.score_lse_rows(qv, np.full(len(qv), sm), kv, np.ones(-(-len(kv) // 64)), rows, causal,
                            score_bias=bias, q_block=1)
     return o1, bound, lse

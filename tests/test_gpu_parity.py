@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import quantized_attention_quant_amd as sage
+import margins
 import workloads
 from oracle import sage_oracle as O
 
@@ -58,6 +59,7 @@ def check_out(ours, o1, o2, label, o2_floor=COS_O2):
     c1 = cos(ours, o1)
     c2 = cos(ours, o2)
     say(f"{label}: max_abs_vs_O1={err:.3e} cos_O1={c1:.6f} cos_O2={c2:.6f}")
+    margins.record(label, err, c1, c2)
     assert err <= MAX_ABS, (label, err)
     assert c1 >= COS_O1, (label, c1)
     assert c2 >= o2_floor, (label, c2)

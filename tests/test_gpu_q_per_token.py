@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import quantized_attention_quant_amd as sage
+import margins
 import workloads
 from oracle import sage_oracle as O
 
@@ -48,6 +49,7 @@ def check_out(ours, o1, o2, label):
     err = np.abs(ours - o1.astype(np.float64)).max()
     c1, c2 = cos(ours, o1), cos(ours, o2)
     say(f"{label}: max_abs_vs_O1={err:.3e} cos_O1={c1:.6f} cos_O2={c2:.6f}")
+    margins.record(label, err, c1, c2)
     assert err <= MAX_ABS, (label, err)
     assert c1 >= COS_O1, (label, c1)
     assert c2 >= COS_O2, (label, c2)
@@ -215,6 +217,7 @@ def test_q_per_token_large_magnitude(causal, d, pv_mode):
         err = np.abs(ours - ref1).max()
         c1, c2o = cos(ours, ref1), cos(ours, ref2)
         say(f"  h={h}: max_abs_vs_O1={err:.3e} cos_O1={c1:.6f} cos_O2={c2o:.6f}")
+        margins.record(f"x-scaled h={h}", err, c1, c2o)
         assert err <= MAX_ABS and c1 >= COS_O1, (h, err, c1)
         # at this magnitude the method itself is further from exact attention
         assert c2o >= min(COS_O2, cos(ref1, ref2) - 1e-4), (h, c2o)
