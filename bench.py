@@ -304,14 +304,21 @@ def main():
     log(f"bench: {args.steps} steps, {ms:.3f} ms/step, {value:.1f} TOPS")
 
     roofline = None
-    if not w.varlen:
+    if True:
         # the fused attention kernel alone, re-run on the workspace the last step filled
         reps = max(args.steps, 5)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, q=q, **opts)
+        if w.varlen:
+            def kernel_only():
+                sage.sage_test_attn_varlen_from_workspace(o, ws, cu, mx, v, is_causal=w.causal, pv_mode=w.pv_mode,
+                                                          q=q, **opts)
+        else:
+            def kernel_only():
+                sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, q=q, **opts)
+        kernel_only()
         e0.record(stream)
         for _ in range(reps):
-            sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, q=q, **opts)
+            kernel_only()
         e1.record(stream)
         torch.cuda.synchronize()
         kern_ms = e0.elapsed_time(e1) / reps

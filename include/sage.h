@@ -262,6 +262,23 @@ sage_status_t sage_test_attn_from_workspace(void* o, const void* q, const void* 
                                             int N, int d, int is_causal, sage_pv_mode_t pv_mode, int options,
                                             const void* workspace, size_t workspace_bytes,
                                             sage_stream_t stream);
+/*
+ * sage_test_attn_varlen_from_workspace: the same for packed variable-length
+ *   sequences (jsqmd "SageAttention完全指南", API list: sageattn_varlen):
+ *   launch only the fused attention kernel on a workspace that a preceding
+ *   sage_attn_varlen_fwd call with the same cu_seqlens, nseq, max_seqlen,
+ *   total_tokens, H, H_kv, d, is_causal, pv_mode and options has filled; o, q
+ *   packed fp16 [H,T,d], v packed fp16 [H_kv,T,d] (q and v with the meaning
+ *   they have above).  Same validation as sage_attn_varlen_fwd; with
+ *   total_tokens = 0 nothing is launched.  Used to time the attention kernel
+ *   alone on the varlen workload.
+ */
+sage_status_t sage_test_attn_varlen_from_workspace(void* o, const void* q, const void* v,
+                                                   const int32_t* cu_seqlens, int nseq, int max_seqlen,
+                                                   int64_t total_tokens, int H, int H_kv, int d,
+                                                   int is_causal, sage_pv_mode_t pv_mode, int options,
+                                                   const void* workspace, size_t workspace_bytes,
+                                                   sage_stream_t stream);
 sage_status_t sage_test_workspace_layout(int varlen, int B, int H, int H_kv, int N,
                                          int64_t total_tokens, int d, sage_pv_mode_t pv_mode,
                                          int options, size_t offsets_out[12]);

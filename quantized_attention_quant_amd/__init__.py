@@ -21,7 +21,7 @@ __all__ = [
     "sage_status_string", "sage_quant_qk_workspace_size", "sage_quant_qk", "sage_quant_v_fp8",
     "sage_attn_workspace_size", "sage_attn_fwd", "sage_attn_varlen_workspace_size",
     "sage_attn_varlen_fwd", "sage_test_workspace_layout", "sage_test_qk_tiles",
-    "sage_test_attn_from_workspace",
+    "sage_test_attn_from_workspace", "sage_test_attn_varlen_from_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,6 +59,9 @@ SIGNATURES = {
     "sage_test_qk_tiles": (_c.c_int, [_P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P, _c.c_int, _P, _P]),
     "sage_test_attn_from_workspace": (_c.c_int, [_P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                                  _c.c_int, _c.c_int, _c.c_int, _P, _c.c_size_t, _P]),
+    "sage_test_attn_varlen_from_workspace": (_c.c_int, [_P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int64, _c.c_int,
+                                                        _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _P,
+                                                        _c.c_size_t, _P]),
 }
 
 
@@ -323,4 +326,29 @@ def sage_test_attn_from_workspace(out: torch.Tensor, workspace: torch.Tensor, v:
                                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                              _stream(stream))
     _check(st, "sage_test_attn_from_workspace")
+    return out
+
+
+def sage_test_attn_varlen_from_workspace(out: torch.Tensor, workspace: torch.Tensor, cu_seqlens: torch.Tensor,
+                                         max_seqlen: int, v: Optional[torch.Tensor] = None,
+                                         is_causal: bool = False, pv_mode: str = "fp16", stream=None,
+                                         H_kv: Optional[int] = None, smooth_q: bool = False,
+                                         q_per_token: bool = False, q: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Run only the fused attention kernel on a workspace filled by
+    sage_attn_varlen_fwd (same cu_seqlens, shapes and options; v, q as for
+    sage_test_attn_from_workspace, packed [H_kv,T,d] / [H,T,d]); out fp16
+    [H,T,d] is written and returned."""
+    _need(out, "out", torch.float16, 3)
+    if v is not None:
+        _need(v, "v", torch.float16, 3)
+    if q is not None:
+        _need(q, "q", torch.float16, 3)
+    nseq, N, T, H, d = _varlen_dims(out, cu_seqlens, max_seqlen)
+    st = lib().sage_test_attn_varlen_from_workspace(out.data_ptr(), 0 if q is None else q.data_ptr(),
+                                                    0 if v is None else v.data_ptr(), cu_seqlens.data_ptr(), nseq,
+                                                    N, T, H, H if H_kv is None else H_kv, d, int(bool(is_causal)),
+                                                    PV_MODES[pv_mode], _options(smooth_q, q_per_token),
+                                                    workspace.data_ptr(),
+                                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "sage_test_attn_varlen_from_workspace")
     return out

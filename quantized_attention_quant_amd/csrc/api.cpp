@@ -280,6 +280,67 @@ sage_status_t varlen_geom(const int32_t* cu, int nseq, int max_seqlen, int64_t t
   return SAGE_OK;
 }
 
+
+// The attention kernel alone on a workspace a preceding forward filled (the
+// sage_test_attn_*from_workspace hooks); g: geometry of Q and O.
+sage_status_t attn_from_workspace(void* o, const void* q, const void* v, const SeqGeom& g, int H_kv, bool varlen,
+                                  int is_causal, sage_pv_mode_t pv_mode, int options, const void* workspace,
+                                  size_t workspace_bytes, sage_stream_t stream) {
+  const int H = g.H, d = g.d;
+  if (!kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!o || !workspace || !aligned16(o) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (!pv_mode_ok(pv_mode)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv_mode == SAGE_PV_FP16 && (!v || !aligned16(v))) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
+  // Q without smoothing: the attention kernel quantises q itself, or, with q
+  // NULL, reads Q̂ and δQ from regions [0] and [2]
+  const bool qfuse = pv_mode != SAGE_MXFP4 && (options & SAGE_OPT_SMOOTH_Q) == 0 && q != nullptr;
+  if (qfuse && !aligned16(q)) return SAGE_ERR_INVALID_ARGUMENT;
+  const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
+  const WsLayout L = make_layout(varlen, g.B, H, H_kv, g.N, g.T, d, pv_mode, options);
+  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
+  const int64_t rows = varlen ? (int64_t)H * g.T : (int64_t)g.B * H * g.N;
+  const size_t tensor_bytes = (size_t)rows * d * 2;
+  const size_t kv_bytes = tensor_bytes / (size_t)H * (size_t)H_kv;
+  if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (pv_mode == SAGE_PV_FP16 && (overlaps(o, tensor_bytes, v, kv_bytes) || overlaps(workspace, L.total, v, kv_bytes)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  if (qfuse && (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(workspace, L.total, q, tensor_bytes)))
+    return SAGE_ERR_INVALID_ARGUMENT;
+  const char* ws = static_cast<const char*>(workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (pv_mode == SAGE_MXFP4) {
+    float sm;
+    resolve_sm_scale(0.f, d, &sm);
+    sage::MxArgs a{reinterpret_cast<const uint8_t*>(ws + L.off[0]), reinterpret_cast<const uint8_t*>(ws + L.off[2]),
+                   reinterpret_cast<const uint8_t*>(ws + L.off[1]), reinterpret_cast<const uint8_t*>(ws + L.off[5]),
+                   reinterpret_cast<const uint8_t*>(ws + L.off[3]), static_cast<uint16_t*>(o), nullptr, g,
+                   H / H_kv, (float)((double)sm * 1.4426950408889634)};
+    if (options & SAGE_OPT_SMOOTH_Q) a.qb_slots = reinterpret_cast<const float*>(ws + L.off[9]);
+    sage::launch_attn_mx(a, is_causal != 0, st);
+    return finish(st);
+  }
+  sage::AttnArgs a{reinterpret_cast<const int8_t*>(ws + L.off[0]), reinterpret_cast<const int8_t*>(ws + L.off[1]),
+                   reinterpret_cast<const float*>(ws + L.off[2]), reinterpret_cast<const float*>(ws + L.off[3]),
+                   fp8 ? reinterpret_cast<const uint8_t*>(ws + L.off[5]) : static_cast<const uint8_t*>(v),
+                   reinterpret_cast<const float*>(ws + L.off[6]), static_cast<uint16_t*>(o), nullptr, g, H / H_kv};
+  a.q_per_token = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
+  if (qfuse) {
+    a.q16 = static_cast<const uint16_t*>(q);
+    resolve_sm_scale(0.f, d, &a.sm_scale);
+  }
+  if (options & SAGE_OPT_SMOOTH_Q) {
+    a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[fp8 ? 10 : 9]);
+    a.qb_fix = reinterpret_cast<const float*>(ws + L.off[10]);
+    a.qb_flags = fp8 ? nullptr : reinterpret_cast<const int32_t*>(ws + L.off[11]);
+    a.qb_any = fp8 ? nullptr : row_summaries(const_cast<char*>(ws) + L.off[11], g.B, H, g.N);
+  }
+  sage::launch_attn(a, is_causal != 0, fp8, st);
+  return finish(st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -437,58 +498,20 @@ sage_status_t sage_test_attn_from_workspace(void* o, const void* q, const void* 
                                             const void* workspace, size_t workspace_bytes, sage_stream_t stream) {
   const sage_status_t s = check_dims(B, H, N, d);
   if (s != SAGE_OK) return s;
-  if (!kv_heads_ok(H, H_kv)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!o || !workspace || !aligned16(o) || (reinterpret_cast<uintptr_t>(workspace) % kWsAlign) != 0)
-    return SAGE_ERR_INVALID_ARGUMENT;
-  if (!pv_mode_ok(pv_mode)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (pv_mode == SAGE_PV_FP16 && (!v || !aligned16(v))) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
-  // Q without smoothing: the attention kernel quantises q itself, or, with q
-  // NULL, reads Q̂ and δQ from regions [0] and [2]
-  const bool qfuse = pv_mode != SAGE_MXFP4 && (options & SAGE_OPT_SMOOTH_Q) == 0 && q != nullptr;
-  if (qfuse && !aligned16(q)) return SAGE_ERR_INVALID_ARGUMENT;
-  const bool fp8 = pv_mode == SAGE_PV_FP8_E4M3;
-  const WsLayout L = make_layout(false, B, H, H_kv, N, 0, d, pv_mode, options);
-  if (workspace_bytes < L.total) return SAGE_ERR_WORKSPACE_TOO_SMALL;
-  const size_t tensor_bytes = (size_t)B * H * N * d * 2;
-  const size_t kv_bytes = tensor_bytes / (size_t)H * (size_t)H_kv;
-  if (overlaps(o, tensor_bytes, workspace, L.total)) return SAGE_ERR_INVALID_ARGUMENT;
-  if (pv_mode == SAGE_PV_FP16 && (overlaps(o, tensor_bytes, v, kv_bytes) || overlaps(workspace, L.total, v, kv_bytes)))
-    return SAGE_ERR_INVALID_ARGUMENT;
-  if (qfuse && (overlaps(o, tensor_bytes, q, tensor_bytes) || overlaps(workspace, L.total, q, tensor_bytes)))
-    return SAGE_ERR_INVALID_ARGUMENT;
-  const char* ws = static_cast<const char*>(workspace);
-  const SeqGeom g{nullptr, B, H, N, d, 0};
-  if (pv_mode == SAGE_MXFP4) {
-    float sm;
-    resolve_sm_scale(0.f, d, &sm);
-    sage::MxArgs a{reinterpret_cast<const uint8_t*>(ws + L.off[0]), reinterpret_cast<const uint8_t*>(ws + L.off[2]),
-                   reinterpret_cast<const uint8_t*>(ws + L.off[1]), reinterpret_cast<const uint8_t*>(ws + L.off[5]),
-                   reinterpret_cast<const uint8_t*>(ws + L.off[3]), static_cast<uint16_t*>(o), nullptr, g,
-                   H / H_kv, (float)((double)sm * 1.4426950408889634)};
-    if (options & SAGE_OPT_SMOOTH_Q) a.qb_slots = reinterpret_cast<const float*>(ws + L.off[9]);
-    sage::launch_attn_mx(a, is_causal != 0, reinterpret_cast<hipStream_t>(stream));
-    return finish(reinterpret_cast<hipStream_t>(stream));
-  }
-  sage::AttnArgs a{reinterpret_cast<const int8_t*>(ws + L.off[0]), reinterpret_cast<const int8_t*>(ws + L.off[1]),
-                   reinterpret_cast<const float*>(ws + L.off[2]), reinterpret_cast<const float*>(ws + L.off[3]),
-                   fp8 ? reinterpret_cast<const uint8_t*>(ws + L.off[5]) : static_cast<const uint8_t*>(v),
-                   reinterpret_cast<const float*>(ws + L.off[6]), static_cast<uint16_t*>(o), nullptr, g, H / H_kv};
-  a.q_per_token = (options & SAGE_OPT_Q_PER_TOKEN) != 0;
-  if (qfuse) {
-    a.q16 = static_cast<const uint16_t*>(q);
-    resolve_sm_scale(0.f, d, &a.sm_scale);
-  }
-  if (options & SAGE_OPT_SMOOTH_Q) {
-    a.qb_slots = reinterpret_cast<const int32_t*>(ws + L.off[fp8 ? 10 : 9]);
-    a.qb_fix = reinterpret_cast<const float*>(ws + L.off[10]);
-    a.qb_flags = fp8 ? nullptr : reinterpret_cast<const int32_t*>(ws + L.off[11]);
-    a.qb_any = fp8 ? nullptr : row_summaries(const_cast<char*>(ws) + L.off[11], B, H, N);
-  }
-  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  sage::launch_attn(a, is_causal != 0, fp8, st);
-  return finish(st);
+  return attn_from_workspace(o, q, v, SeqGeom{nullptr, B, H, N, d, 0}, H_kv, false, is_causal, pv_mode, options,
+                             workspace, workspace_bytes, stream);
+}
+
+sage_status_t sage_test_attn_varlen_from_workspace(void* o, const void* q, const void* v, const int32_t* cu_seqlens,
+                                                   int nseq, int max_seqlen, int64_t total_tokens, int H, int H_kv,
+                                                   int d, int is_causal, sage_pv_mode_t pv_mode, int options,
+                                                   const void* workspace, size_t workspace_bytes,
+                                                   sage_stream_t stream) {
+  SeqGeom g;
+  const sage_status_t s = varlen_geom(cu_seqlens, nseq, max_seqlen, total_tokens, H, d, &g);
+  if (s != SAGE_OK) return s;
+  if (total_tokens == 0) return SAGE_OK;
+  return attn_from_workspace(o, q, v, g, H_kv, true, is_causal, pv_mode, options, workspace, workspace_bytes, stream);
 }
 
 sage_status_t sage_test_qk_tiles(const int8_t* q_int8, const int8_t* k_int8, int B, int H, int N, int d,

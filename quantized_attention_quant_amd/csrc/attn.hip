@@ -1348,8 +1348,10 @@ void launch_attn_mx(const MxArgs& a, bool causal, hipStream_t st) {
 #undef SAGE_MX
 }
 
-// Test hook: the int32 Q̂K̂ᵀ tiles computed by the same tile DMA and QKᵀ device
-// code as the attention kernel.
+// Test hook: the int32 Q̂K̂ᵀ tiles computed by the attention kernel's own tile
+// DMA and matrix phase (matrix_both, FP16 PV: the K̂ fragment offsets computed
+// once, the accumulator start value held in registers at d=128), with a zero
+// P against the zero V half of the stage, so that only the QKᵀ part counts.
 template <int D>
 __global__ __launch_bounds__(kThreads) void qk_tiles_kernel(const int8_t* __restrict__ q, const int8_t* __restrict__ k,
                                                             int B, int H, int N, const int32_t* __restrict__ list,
@@ -1371,10 +1373,34 @@ __global__ __launch_bounds__(kThreads) void qk_tiles_kernel(const int8_t* __rest
   wait_dma_and_sync<0>();
   v4i qf[D / 32];
   load_q_frags<D>(qf, q + row0 * D, qb * kQBlock + 32 * w + r32, N, gg);
-  v4i kf[2][D / 32];
-  load_k_frags<D>(reinterpret_cast<const v4i*>(smem), kf, r32, gg);
+  int kofs[D / 32];
+  k_frag_offsets<D>(r32, gg, kofs);
+  v16i mg;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    int m = kMagicI;
+    if (D == 128) asm volatile("" : "+v"(m));
+    mg[i] = m;
+  }
+  v8h pk16[4];
+  v16f O[D / 32];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) pk16[kc] = v8h{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) O[dt][i] = 0.f;
+  const v8i pk8 = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   v16i S[2];
-  qk_half<D>(kf, qf, S);
+  matrix_both<D, false, false>(smem, kofs, smem + G::KBYTES, lane, gg, qf, S, pk16, pk8, O, nullptr,
+                               D == 128 ? &mg : nullptr);
+  // keep the whole (zero) PV result live so that the phase is compiled as in the forward
+  float z = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) z += O[dt][i];
+  if (z != 0.f) o[0] = -1;
 #pragma unroll
   for (int s = 0; s < 2; ++s)
 #pragma unroll
