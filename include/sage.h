@@ -33,7 +33,8 @@
  *   - Supported head dims: d = 64 or d = 128.
  *   - Ownership: the caller allocates and frees every buffer, the workspace
  *     included.  The library never allocates or frees device memory and keeps
- *     no pointer after a call returns.
+ *     no pointer after a call returns; its only device memory of its own is
+ *     the static scratch array of sage_attn_fwd_noalloc.
  *   - Asynchrony: calls only enqueue work on `stream` (a hipStream_t; NULL is
  *     the null stream) and return without synchronising.  Buffers must stay
  *     valid until the stream has completed the work.
@@ -46,7 +47,8 @@
  *     SAGE_ERR_DEVICE.  No C++ exception crosses this boundary.
  *   - Inputs must be finite; the contents of cu_seqlens must satisfy the
  *     documented constraints (they live on the device and are not checked).
- *   - Calls are reentrant; the library holds no mutable global state.
+ *   - Calls are reentrant; the library holds no mutable global state, apart
+ *     from the per-GPU scratch array of sage_attn_fwd_noalloc (see there).
  */
 #ifndef SAGE_H_
 #define SAGE_H_
@@ -182,6 +184,29 @@ sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o
                             int B, int H, int H_kv, int N, int d, sage_layout_t layout,
                             int is_causal, sage_pv_mode_t pv_mode, int options, float sm_scale,
                             void* workspace, size_t workspace_bytes, sage_stream_t stream);
+
+/* ------------------------------------------------------------------------
+ * sage_attn_fwd_noalloc — sage_attn_fwd without a workspace argument, for
+ *   callers that cannot allocate device memory (code under HIP graph capture,
+ *   tight serving loops, harnesses that forbid allocation).  Same arguments,
+ *   semantics, outputs and validation as sage_attn_fwd; the pre-pass results
+ *   go to a scratch array the library owns: SAGE_NOALLOC_SCRATCH_BYTES of
+ *   device memory per GPU, reserved when the library's code is loaded on that
+ *   GPU and held until the process ends.  Problems whose
+ *   sage_attn_workspace_size exceeds it -> SAGE_ERR_WORKSPACE_TOO_SMALL
+ *   (call sage_attn_fwd with a workspace instead); SAGE_ERR_DEVICE if the
+ *   scratch array cannot be located on the current device.  The call
+ *   allocates and frees nothing.  Every call on one GPU shares that GPU's
+ *   array (the pre-pass rewrites it; nothing is assumed about its contents on
+ *   entry): calls that overlap on one GPU — on different streams, or from
+ *   different host threads without ordering — race, and their results are
+ *   undefined; calls on one stream are ordered and safe.
+ */
+#define SAGE_NOALLOC_SCRATCH_BYTES (256u << 20)
+sage_status_t sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int B, int H, int H_kv, int N, int d, sage_layout_t layout,
+                                    int is_causal, sage_pv_mode_t pv_mode, int options, float sm_scale,
+                                    sage_stream_t stream);
 
 /* ------------------------------------------------------------------------
  * sage_attn_varlen_fwd — forward on packed variable-length sequences.

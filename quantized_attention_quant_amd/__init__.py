@@ -19,7 +19,7 @@ import torch
 __all__ = [
     "SageError", "LIB_PATH", "lib", "PV_MODES",
     "sage_status_string", "sage_quant_qk_workspace_size", "sage_quant_qk", "sage_quant_v_fp8",
-    "sage_attn_workspace_size", "sage_attn_fwd", "sage_attn_varlen_workspace_size",
+    "sage_attn_workspace_size", "sage_attn_fwd", "sage_attn_fwd_noalloc", "sage_attn_varlen_workspace_size",
     "sage_attn_varlen_fwd", "sage_test_workspace_layout", "sage_test_qk_tiles",
     "sage_test_attn_from_workspace", "sage_test_attn_varlen_from_workspace",
 ]
@@ -49,6 +49,8 @@ SIGNATURES = {
                                                _c.c_int]),
     "sage_attn_fwd": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
                                  _c.c_int, _c.c_int, _c.c_int, _c.c_float, _P, _c.c_size_t, _P]),
+    "sage_attn_fwd_noalloc": (_c.c_int, [_P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_int,
+                                         _c.c_int, _c.c_int, _c.c_int, _c.c_int, _c.c_float, _P]),
     "sage_attn_varlen_workspace_size": (_c.c_size_t, [_c.c_int, _c.c_int, _c.c_int64, _c.c_int, _c.c_int,
                                                       _c.c_int, _c.c_int, _c.c_int]),
     "sage_attn_varlen_fwd": (_c.c_int, [_P, _P, _P, _P, _P, _P, _c.c_int, _c.c_int, _c.c_int64, _c.c_int,
@@ -242,6 +244,35 @@ def sage_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: 
                          LAYOUT_HND, int(bool(is_causal)), PV_MODES[pv_mode], opts, float(sm_scale),
                          ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
     _check(st, "sage_attn_fwd")
+    return o if lse_t is None else (o, lse_t)
+
+
+NOALLOC_SCRATCH_BYTES = 256 << 20   # SAGE_NOALLOC_SCRATCH_BYTES of include/sage.h
+
+
+def sage_attn_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, is_causal: bool = False,
+                          pv_mode: str = "fp16", sm_scale: float = 0.0, out: Optional[torch.Tensor] = None,
+                          stream=None, return_lse: bool = False, lse: Optional[torch.Tensor] = None,
+                          smooth_q: bool = False, q_per_token: bool = False):
+    """sage_attn_fwd without a workspace: the library's per-GPU scratch array
+    holds the pre-pass results (calls that overlap on one GPU race).  Returns
+    o fp16 [B,H,N,d], or (o, lse)."""
+    L = lib()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t, name, torch.float16, 4)
+    B, H, N, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2:] != q.shape[2:]:
+        raise ValueError("k and v must be [B,H_kv,N,d] with q's B, N and d")
+    H_kv = k.shape[1]
+    if pv_mode not in PV_MODES:
+        raise ValueError(f"pv_mode must be one of {list(PV_MODES)}")
+    o = torch.empty_like(q) if out is None else out
+    _need(o, "out", torch.float16, 4)
+    lse_t = _lse_out(return_lse, lse, (B, H, N), q.device)
+    st = L.sage_attn_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), _ptr(lse_t), B, H, H_kv, N,
+                                 d, LAYOUT_HND, int(bool(is_causal)), PV_MODES[pv_mode],
+                                 _options(smooth_q, q_per_token), float(sm_scale), _stream(stream))
+    _check(st, "sage_attn_fwd_noalloc")
     return o if lse_t is None else (o, lse_t)
 
 

@@ -6,8 +6,16 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 
 #include "sage_internal.h"
+
+// Scratch of the allocation-free forward (sage_attn_fwd_noalloc): a device
+// array the library owns, one copy per GPU, living until the process ends.
+// Host code never passes the array's name to a kernel (in host code it is only
+// a stand-in for the symbol): it looks up each device's copy once with
+// hipGetSymbolAddress and passes that address.
+static __device__ __align__(256) unsigned char scratch[SAGE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -341,6 +349,22 @@ sage_status_t attn_from_workspace(void* o, const void* q, const void* v, const S
   return finish(st);
 }
 
+// Device address of this device's copy of the scratch array, looked up once
+// per device (with that device current) and kept; nullptr if the lookup fails.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_ptr[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess ? p : nullptr;
+  });
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -455,6 +479,23 @@ sage_status_t sage_attn_fwd(const void* q, const void* k, const void* v, void* o
   const SeqGeom g{nullptr, B, H, N, d, 0};
   return attn_forward(q, k, v, o, lse, g, H_kv, false, is_causal, pv_mode, options, sm_scale, workspace,
                       workspace_bytes, stream);
+}
+
+sage_status_t sage_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                    int H_kv, int N, int d, sage_layout_t layout, int is_causal,
+                                    sage_pv_mode_t pv_mode, int options, float sm_scale, sage_stream_t stream) {
+  if (layout != SAGE_LAYOUT_HND) return layout < 0 ? SAGE_ERR_INVALID_ARGUMENT : SAGE_ERR_UNSUPPORTED;
+  const sage_status_t s = check_dims(B, H, N, d);
+  if (s != SAGE_OK) return s;
+  if (!kv_heads_ok(H, H_kv) || !pv_mode_ok(pv_mode) || !options_known(options)) return SAGE_ERR_INVALID_ARGUMENT;
+  if (!mode_options_supported(pv_mode, options)) return SAGE_ERR_UNSUPPORTED;
+  if (make_layout(false, B, H, H_kv, N, 0, d, pv_mode, options).total > (size_t)SAGE_NOALLOC_SCRATCH_BYTES)
+    return SAGE_ERR_WORKSPACE_TOO_SMALL;  // beyond the scratch array: use sage_attn_fwd with a workspace
+  void* ws = scratch_for_current_device();
+  if (!ws) return SAGE_ERR_DEVICE;
+  const SeqGeom g{nullptr, B, H, N, d, 0};
+  return attn_forward(q, k, v, o, lse, g, H_kv, false, is_causal, pv_mode, options, sm_scale, ws,
+                      (size_t)SAGE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t sage_attn_varlen_workspace_size(int nseq, int max_seqlen, int64_t total_tokens, int H, int H_kv, int d,

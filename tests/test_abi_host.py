@@ -208,6 +208,21 @@ def test_attn_from_workspace_rejects_aliasing():
     assert f(*bad) == INVALID
 
 
+def test_noalloc_rejects_before_any_device_call():
+    L = sage.lib()
+    def fwd(B=1, H=2, Hkv=2, N=256, d=64, layout=0, pv=0, opt=0):
+        return L.sage_attn_fwd_noalloc(ALIGNED, ALIGNED * 2, ALIGNED * 3, ALIGNED * 4, None, B, H, Hkv, N, d, layout,
+                                       0, pv, opt, 0.0, None)
+    assert fwd(d=96) == INVALID
+    assert fwd(layout=1) == UNSUPPORTED
+    assert fwd(Hkv=3) == INVALID
+    assert fwd(pv=3) == INVALID
+    assert fwd(opt=3) == UNSUPPORTED
+    # a workspace beyond the scratch array: the caller must pass one instead
+    assert sage.sage_attn_workspace_size(1, 64, 32768, 128) > sage.NOALLOC_SCRATCH_BYTES
+    assert fwd(H=64, Hkv=64, N=32768, d=128) == WS_SMALL
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(sage, "_lib", None)
     monkeypatch.setattr(sage, "LIB_PATH", str(tmp_path / "missing.so"))
