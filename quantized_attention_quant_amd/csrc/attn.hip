@@ -900,12 +900,20 @@ void attn_fwd_kernel(AttnArgs a) {
   // One workgroup barrier per tile.  Group A runs matrix(t) then softmax(t),
   // group B softmax(t-1) then matrix(t), so on each SIMD one wave's MFMAs
   // overlap the other wave's exponentials; matrix(t) = PV of tile t-1 and QKᵀ
-  // of tile t.
+  // of tile t.  Where a softmax outlasts a matrix phase (FP8 PV, d = 64), the
+  // two softmaxes of a SIMD overlap and share its VALU; group B's is the one
+  // the barrier waits on (its matrix phase still follows), so it issues at a
+  // raised wave priority and group A's softmax takes the slack.
+  constexpr bool kRaiseSoftB = FP8 || D == 64;
   for (int t = 0; t < ntiles; ++t) {
     if (lead && t + kAhead < ntiles)
       issue_tile<D, FP8, kThreads, SM>(kbase, kbytes, vbase, vbytes, t + kAhead,
                                        smem + ((t + kAhead) % kRingStages) * G::STAGE, w, lane, ss);
-    if (!lead && t > 0) softmax_step(t - 1);
+    if (!lead && t > 0) {
+      if (kRaiseSoftB) __builtin_amdgcn_s_setprio(1);
+      softmax_step(t - 1);
+      if (kRaiseSoftB) __builtin_amdgcn_s_setprio(0);
+    }
     // One place for both MFMA parts keeps O and S in fixed registers.  At t = 0
     // the pending P is zero (O += 0·V of tile 0, which has landed); at t = nact
     // the QKᵀ result is not used.
@@ -1279,11 +1287,18 @@ void attn_mx_kernel(MxArgs a) {
       mx_softmax<D>(c, a.c2);
     }
   };
+  // The MXFP4 softmax (exact tile max, per-block P scales) outlasts the
+  // matrix phase: group B's softmax issues at a raised wave priority, as in
+  // attn_fwd_kernel.
   for (int t = 0; t < ntiles; ++t) {
     if (lead && t + kAhead < ntiles)
       issue_mx_tile<D, SM>(kbase, kbytes, vbase, vbytes, abase, abytes, t + kAhead,
                            smem + ((t + kAhead) % kRingStages) * G::STAGE, w, lane, ss);
-    if (!lead && t > 0) softmax_step(t - 1);
+    if (!lead && t > 0) {
+      __builtin_amdgcn_s_setprio(1);
+      softmax_step(t - 1);
+      __builtin_amdgcn_s_setprio(0);
+    }
     if (t <= nact && nact > 0) {
       const char* cur = smem + (t % kRingStages) * G::STAGE;
       const char* prev = smem + ((t == 0 ? 0 : t - 1) % kRingStages) * G::STAGE;
