@@ -166,7 +166,9 @@ sage_status_t sage_quant_v_fp8(const void* v, int B, int H, int N, int d, sage_l
  *   SAGE_OPT_Q_PER_TOKEN -> SAGE_ERR_UNSUPPORTED).  options (sage_option_t bits):
  *   SAGE_OPT_SMOOTH_Q — Q̂ and δQ come from Q minus its block mean and every
  *   score of a row of block b gets sm_scale·q̄_b·(k_j − km) added back
- *   (carried within one unit of δQ·δK; the workspace is then larger);
+ *   (FP16 PV: carried within one unit of δQ·δK in the accumulator's start
+ *   value, in fp32 for the rare half tiles it does not fit; FP8 PV and MXFP4:
+ *   added in fp32 to every score; the workspace is then larger);
  *   SAGE_OPT_Q_PER_TOKEN — one Q scale per query row.  sm_scale <= 0 ->
  *   1/sqrt(d).
  *   The pre-pass (smoothing, quantisation, V packing) writes into the
