@@ -219,6 +219,11 @@ def main():
     ap.add_argument("--smooth-q", action="store_true",
                     help="time the forward with Q smoothing (the score term of Q's block mean added back)")
     ap.add_argument("--q-per-token", action="store_true", help="time the forward with per-token Q scales")
+    ap.add_argument("--kv-heads", type=int, default=0, metavar="H_KV",
+                    help="grouped-query attention: K and V with H_KV heads (the workload's first H_KV), "
+                         "H_KV dividing H")
+    ap.add_argument("--lse", action="store_true",
+                    help="the forward also writes the per-row log-sum-exp (the kernel-only time omits it)")
     ap.add_argument("--mxfp4", action="store_true",
                     help="time the forward in MXFP4 mode (QK and PV in microscaling FP4) instead of the "
                          "workload's PV mode")
@@ -263,13 +268,25 @@ def main():
         w = dataclasses.replace(w, pv_mode="mxfp4")
     sq, qt = bool(args.smooth_q), bool(args.q_per_token)
     opts = dict(smooth_q=sq, q_per_token=qt)
+    hkv = args.kv_heads or w.H
+    if hkv <= 0 or w.H % hkv:
+        raise SystemExit(f"--kv-heads {hkv} must divide H = {w.H}")
+    if hkv != w.H and w.varlen:
+        raise SystemExit("--kv-heads is timed on the dense workloads")
     log(f"bench: workload {w.name}: {w.description}" + (" (Q smoothing)" if sq else "") +
-        (" (per-token Q scales)" if qt else ""))
+        (" (per-token Q scales)" if qt else "") + (f" (H_kv = {hkv})" if hkv != w.H else "") +
+        (" (with lse)" if args.lse else ""))
     x = workloads.generate(w)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q, k, v = (torch.from_numpy(a).to(dev) for a in (x.q, x.k, x.v))
+    if hkv != w.H:
+        # grouped-query attention: the first H_kv heads of the workload's K and V
+        k, v = k[:, :hkv].contiguous(), v[:, :hkv].contiguous()
     o = torch.empty_like(q)
+    lse = None
+    if args.lse:
+        lse = torch.empty(tuple(q.shape[:-1]), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     if w.varlen:
         cu = torch.from_numpy(x.cu_seqlens).to(dev)
@@ -280,13 +297,13 @@ def main():
 
         def step():
             sage.sage_attn_varlen_fwd(q, k, v, cu, mx, is_causal=w.causal, pv_mode=w.pv_mode, out=o, workspace=ws,
-                                      **opts)
+                                      lse=lse, **opts)
     else:
-        ws = torch.empty(sage.sage_attn_workspace_size(w.B, w.H, w.N, w.d, w.pv_mode, **opts),
+        ws = torch.empty(sage.sage_attn_workspace_size(w.B, w.H, w.N, w.d, w.pv_mode, H_kv=hkv, **opts),
                          dtype=torch.uint8, device=dev)
 
         def step():
-            sage.sage_attn_fwd(q, k, v, is_causal=w.causal, pv_mode=w.pv_mode, out=o, workspace=ws, **opts)
+            sage.sage_attn_fwd(q, k, v, is_causal=w.causal, pv_mode=w.pv_mode, out=o, workspace=ws, lse=lse, **opts)
 
     ops = attn_ops(w, x.lengths)
     for _ in range(args.warmup):
@@ -314,7 +331,8 @@ def main():
                                                           q=q, **opts)
         else:
             def kernel_only():
-                sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, q=q, **opts)
+                sage.sage_test_attn_from_workspace(o, ws, v, is_causal=w.causal, pv_mode=w.pv_mode, q=q, H_kv=hkv,
+                                                   **opts)
         kernel_only()
         e0.record(stream)
         for _ in range(reps):
@@ -324,7 +342,7 @@ def main():
         kern_ms = e0.elapsed_time(e1) / reps
         achieved = ops / (kern_ms * 1e-3) / 1e12
         traffic = measured_traffic(w.name + ("+mxfp4" if w.pv_mode == "mxfp4" else "") + ("+smooth_q" if sq else "")
-                                   + ("+q_per_token" if qt else ""))
+                                   + ("+q_per_token" if qt else "") + (f"+kv{hkv}" if hkv != w.H else ""))
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic,
                     "kernel": f"{'attn_mx_kernel' if w.pv_mode == 'mxfp4' else 'attn_fwd_kernel'}<{w.d},{w.pv_mode}"
@@ -337,12 +355,13 @@ def main():
             f"({100 * achieved / INT8_PEAK_TOPS:.1f}% of INT8 peak)")
 
     cpu = None
-    if not args.no_cpu_baseline and w.pv_mode != "mxfp4" and not (sq or qt):
+    if not args.no_cpu_baseline and w.pv_mode != "mxfp4" and not (sq or qt) and hkv == w.H and not args.lse:
         log("bench: timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(w, x)
 
     config = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "causal": w.causal,
-              "pv_mode": w.pv_mode, "smooth_q": sq, "q_per_token": qt, "description": w.description}
+              "pv_mode": w.pv_mode, "smooth_q": sq, "q_per_token": qt, "H_kv": hkv, "lse": bool(args.lse),
+              "description": w.description}
     if w.varlen:
         config["lengths"] = [int(n) for n in x.lengths]
     rec = {

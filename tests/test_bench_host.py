@@ -1,5 +1,6 @@
-"""bench.py's host-side contract, without a GPU: one GPU only, and the
-rocprofv3 summary reader on a database written here."""
+"""bench.py's host-side contract, without a GPU: one GPU only, the
+grouped-query option's check, and the rocprofv3 summary reader on a database
+written here."""
 import os
 import sqlite3
 import subprocess
@@ -15,6 +16,14 @@ def test_more_than_one_gpu_exits_with_a_message():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_kv_heads_must_divide_the_query_heads():
+    # checked before any input is generated or a device is touched
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--kv-heads", "7"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0
+    assert "must divide H = 40" in (r.stdout + r.stderr)
 
 
 def test_rocprof_summary_reads_kernel_rows(tmp_path):
