@@ -164,6 +164,50 @@ def test_quant_zero_blocks_and_constant_k():
     assert np.abs(o[0, 0].astype(np.float64) - want).max() < 2e-3
 
 
+def _zero_scale_inputs(seed, n=320, d=128, H=2):
+    """K whose token mean is exactly c, with keys 64..127 equal to c (after
+    smoothing that block is zero: δK = 0), and Q with its second 128-row block
+    zero (δQ = 0).  Values are multiples of 1/16 below 8 in magnitude, so every
+    sum is exact in fp16 and fp64."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, H, n, d)).astype(np.float16)
+    q[:, :, 128:256] = 0
+    k = np.empty((1, H, n, d), np.float16)
+    others = np.concatenate([np.arange(64), np.arange(128, n)])
+    for h in range(H):
+        c = rng.integers(-16, 17, d) / 4.0
+        k[0, h, 64:128] = c
+        e = rng.integers(-32, 33, (len(others) // 2, d)) / 16.0
+        pairs = np.concatenate([c + e, c - e])
+        k[0, h, others] = pairs[rng.permutation(len(others))]
+    v = rng.standard_normal((1, H, n, d)).astype(np.float16)
+    return q, k, v
+
+
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_blocks_in_attention(causal, pv_mode):
+    # a K block with δK = 0 and a Q block with δQ = 0 among ordinary blocks:
+    # their scores are exactly 0, which the kernel forms with the smallest
+    # normal factor in place of a zero one
+    say(f"case zero-scale blocks causal={causal} pv={pv_mode}")
+    q, k, v = _zero_scale_inputs(11 + causal)
+    n = q.shape[2]
+    quant = O.quant_qk_dense(q, k)
+    assert (quant["k_scale"][0, :, 1] == 0).all() and (quant["q_scale"][0, :, 1] == 0).all()
+    o = host(sage.sage_attn_fwd(dev(q), dev(k), dev(v), is_causal=causal, pv_mode=pv_mode))
+    vc, vs = O.quant_v_fp8(v)
+    rows = np.arange(n)
+    for h in range(q.shape[1]):
+        qi, qs, ki, ks = O.head_views_dense(quant, 0, h)
+        if pv_mode == "fp8":
+            o1 = O.sage_attention_rows(qi, qs, ki, ks, vc[0, h], rows, causal, "fp8", vs[0, h])
+        else:
+            o1 = O.sage_attention_rows(qi, qs, ki, ks, v[0, h], rows, causal, "fp16")
+        o2 = O.sdpa_fp64_rows(q[0, h], k[0, h], v[0, h], rows, causal)
+        check_out(o[0, h], o1, o2, f"zero-scale blocks h={h}")
+
+
 def test_quant_v_fp8_bit_exact_small():
     say("case quant v fp8 small")
     rng = np.random.default_rng(3)
