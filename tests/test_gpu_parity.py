@@ -208,6 +208,30 @@ def test_zero_scale_blocks_in_attention(causal, pv_mode):
         check_out(o[0, h], o1, o2, f"zero-scale blocks h={h}")
 
 
+@pytest.mark.parametrize("sm_scale", [0.02, 0.3])
+@pytest.mark.parametrize("pv_mode", ["fp16", "fp8"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d", [(200, 64), (257, 128)])
+def test_caller_softmax_scale(n, d, causal, pv_mode, sm_scale):
+    # a softmax scale other than 1/sqrt(d): folded into δQ by the kernel's own
+    # Q quantisation, as the oracle folds it into the pre-pass scale
+    say(f"case sm_scale={sm_scale} n={n} d={d} causal={causal} pv={pv_mode}")
+    x = workloads.generate_custom(300 + n + d, 1, 2, n, d, k_bias=3.0, q_bias=1.0)
+    o = host(sage.sage_attn_fwd(dev(x.q), dev(x.k), dev(x.v), is_causal=causal, pv_mode=pv_mode,
+                                sm_scale=sm_scale))
+    quant = O.quant_qk_dense(x.q, x.k, sm_scale=sm_scale)
+    vc, vs = O.quant_v_fp8(x.v)
+    rows = np.arange(n)
+    for h in range(2):
+        qi, qs, ki, ks = O.head_views_dense(quant, 0, h)
+        if pv_mode == "fp8":
+            o1 = O.sage_attention_rows(qi, qs, ki, ks, vc[0, h], rows, causal, "fp8", vs[0, h])
+        else:
+            o1 = O.sage_attention_rows(qi, qs, ki, ks, x.v[0, h], rows, causal, "fp16")
+        o2 = O.sdpa_fp64_rows(x.q[0, h], x.k[0, h], x.v[0, h], rows, causal, sm_scale=sm_scale)
+        check_out(o[0, h], o1, o2, f"sm_scale={sm_scale} n={n} d={d} h={h}")
+
+
 def test_quant_v_fp8_bit_exact_small():
     say("case quant v fp8 small")
     rng = np.random.default_rng(3)
