@@ -407,7 +407,7 @@ def _nearest_e4m3(x, table):
 
 def test_fp8_p_codes_between_zero_and_one():
     """The FP8 P step for 0 < p < 1 ([DT] "SageAttention 2": P in FP8; the
-    static ×448 scale and the online schedule are this build's readings): one
+    static ×448 scale and the online schedule are readings of that passage): one
     query, integer scores a_j/32 chosen so that 448·p lands between e4m3
     values where round-to-nearest and truncation differ, over two 64-key tiles
     whose second one raises the row max.  Expected output by hand from the
